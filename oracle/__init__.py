@@ -1,0 +1,131 @@
+"""CPU reference ("oracle") for variable-length paged decode attention.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+benchmark's CPU-baseline leg may import this package. The product path (the
+HIP library and its binding) never imports, links or calls it, and this
+package imports nothing from the product.
+
+``decode`` is the fp64 definition of one decode-attention step (C, in
+``oracle.c``); ``plan`` is the integer tile-plan specification the GPU planner
+must reproduce byte for byte; ``brute`` holds an independent NumPy two-pass
+softmax used to pin ``decode`` on tiny inputs. Inputs are plain host arrays
+(numpy, or CPU torch tensors), duck-typed on the attribute names of a decode
+step: B, Hq, Hkv, D, P, num_pages, kv_dtype, q, k_cache, v_cache, k_scale,
+v_scale, page_table, lengths, sm_scale.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+ELEN, EPAGE = -2, -3
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b
+            _b.build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        i32 = ctypes.c_int32
+        lib.oracle_decode.restype = i32
+        lib.oracle_decode.argtypes = [i32] * 8 + [P] * 7 + [ctypes.c_double, P, i32, P, P, i32]
+        lib.oracle_plan.restype = i32
+        lib.oracle_plan.argtypes = [i32] * 8 + [P] * 8
+        lib.oracle_bf16_to_f64.restype = ctypes.c_double
+        lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.oracle_e4m3fn_to_f64.restype = ctypes.c_double
+        lib.oracle_e4m3fn_to_f64.argtypes = [ctypes.c_uint8]
+        _lib = lib
+    return _lib
+
+
+def _np(x, dtype):
+    """Host array view with the given dtype (bit reinterpretation for 16/8-bit)."""
+    if hasattr(x, "detach"):  # torch tensor
+        import torch
+        x = x.detach().cpu().contiguous()
+        if x.dtype == torch.bfloat16:
+            x = x.view(torch.int16)
+        elif x.dtype == getattr(torch, "float8_e4m3fn", None):
+            x = x.view(torch.uint8)
+        x = x.numpy()
+    a = np.ascontiguousarray(x)
+    if a.dtype.itemsize == np.dtype(dtype).itemsize and a.dtype.kind in "iu" and np.dtype(dtype).kind in "iu":
+        return a.view(dtype)
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+
+def bf16_to_f64(bits: int) -> float:
+    return _load().oracle_bf16_to_f64(int(bits) & 0xFFFF)
+
+
+def e4m3fn_to_f64(code: int) -> float:
+    return _load().oracle_e4m3fn_to_f64(int(code) & 0xFF)
+
+
+def decode(case, req_ids=None, threads=0, *, lengths=None, page_table=None, sm_scale=None,
+           q=None, k_cache=None, v_cache=None, k_scale=None, v_scale=None):
+    """fp64 decode attention. Returns (out [n, Hq, D], lse [n, Hq]) float64 for
+    the requests in ``req_ids`` (all, in order, if None). Keyword arguments
+    override the corresponding attributes of ``case``."""
+    lib = _load()
+    lengths = _np(case.lengths if lengths is None else lengths, np.int32)
+    pt = _np(case.page_table if page_table is None else page_table, np.int32)
+    q = _np(case.q if q is None else q, np.uint16)
+    fp8 = case.kv_dtype == "fp8"
+    kdt = np.uint8 if fp8 else np.uint16
+    kc = _np(case.k_cache if k_cache is None else k_cache, kdt)
+    vc = _np(case.v_cache if v_cache is None else v_cache, kdt)
+    ks = vs = None
+    if fp8:
+        ks = _np(case.k_scale if k_scale is None else k_scale, np.float32)
+        vs = _np(case.v_scale if v_scale is None else v_scale, np.float32)
+    B, Hq = int(case.B), int(case.Hq)
+    if req_ids is None:
+        ids = None
+        n = B
+    else:
+        ids = np.ascontiguousarray(req_ids, np.int32)
+        n = len(ids)
+    out = np.zeros((n, Hq, case.D), np.float64)
+    lse = np.zeros((n, Hq), np.float64)
+    rc = lib.oracle_decode(B, Hq, case.Hkv, case.D, case.P, case.num_pages, pt.shape[1], int(fp8),
+                           _ptr(q), _ptr(kc), _ptr(vc), _ptr(ks), _ptr(vs), _ptr(pt), _ptr(lengths),
+                           float(case.sm_scale if sm_scale is None else sm_scale),
+                           _ptr(ids), n, _ptr(out), _ptr(lse), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_decode failed with code {rc}")
+    return out, lse
+
+
+def plan(mode, lengths, Hkv, P, pt_stride, T, W, S=0):
+    """Integer tile plan (mode 0 dynamic, 1 static). Returns a dict of int32 arrays."""
+    lib = _load()
+    lengths = _np(lengths, np.int32)
+    B = len(lengths)
+    out = {
+        "header": np.zeros(8, np.int32),
+        "len_eff": np.zeros(B, np.int32),
+        "tiles_prefix": np.zeros(B + 1, np.int32),
+        "seg_prefix": np.zeros(B * Hkv + 1, np.int32),
+        "first_wg": np.zeros(B * Hkv, np.int32),
+        "wg_begin": np.zeros(W + 1, np.int32),
+        "wg_start_b": np.zeros(W, np.int32),
+    }
+    rc = lib.oracle_plan(int(mode), B, Hkv, P, pt_stride, T, W, int(S), _ptr(lengths),
+                         *[_ptr(out[k]) for k in ("header", "len_eff", "tiles_prefix", "seg_prefix",
+                                                  "first_wg", "wg_begin", "wg_start_b")])
+    if rc != 0:
+        raise ValueError(f"oracle_plan failed with code {rc}")
+    return out

@@ -1,0 +1,341 @@
+/*
+ * CPU reference ("oracle") for variable-length paged decode attention.
+ *
+ * TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg may load this library. The product path never calls it,
+ * and it shares no code, header, table or helper with the HIP path.
+ *
+ * What it computes. One decode step: each request b has one query per query
+ * head and attends to all L_b cached key/value rows of its kv head. The KV cache
+ * is split into pages; the source article only says the cache holds earlier
+ * attention state and that longer histories mean more cached data to read
+ * [Tencent HPC lands in SGLang, challenging default inference kernels, sec.
+ * "Why Tencent HPC matters for online model serving"]. Splitting the KV work
+ * into tiles and merging partial softmax states (the "split-k" the same section
+ * names) is an exact re-association of softmax, so the oracle is the plain
+ * definition written out in fp64, for request b, query head h, kv head
+ * g = h / (Hq/Hkv), L = L_b:
+ *
+ *   K_j = K[page_table[b][j / P]][g][j % P][:],  V_j likewise,  j = 0..L-1
+ *   s_j = sm_scale * sum_d q[b][h][d] * K_j[d]
+ *   m   = max_j s_j,   l = sum_j exp(s_j - m)
+ *   o[b][h][:] = sum_j exp(s_j - m) * V_j / l,   lse[b][h] = m + ln l
+ *
+ * An empty request (L = 0) gives o = 0 and lse = -inf. bf16 values widen
+ * exactly to fp64. fp8 caches hold OCP e4m3fn codes; a code is decoded exactly
+ * and multiplied, in fp64, by the fp32 scale of its (request, kv head).
+ *
+ * The planner below is the integer specification of the per-step tile plan:
+ * uniform tiles handed to workgroups, rebuilt from the current lengths
+ * [same page and section: the scheduler that splits requests into uniform
+ * tiles and hands them to CTAs, remapped as lengths change], and the static
+ * split-k comparison point [same section]. The GPU planner must reproduce its
+ * arrays byte for byte.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---------------------------------------------------------------- values -- */
+
+/* bfloat16 bit pattern -> double (exact: bf16 is the top half of a float). */
+double oracle_bf16_to_f64(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* OCP 8-bit floating point, E4M3 ("e4m3fn"): 1 sign bit, 4 exponent bits with
+ * bias 7, 3 mantissa bits; no infinities; S.1111.111 is NaN; exponent field 0
+ * encodes subnormals m/8 * 2^-6. */
+double oracle_e4m3fn_to_f64(uint8_t c)
+{
+    int sign = c >> 7, e = (c >> 3) & 0xF, m = c & 0x7;
+    double v;
+    if (e == 0xF && m == 0x7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);          /* (m/8) * 2^(1-7) */
+    else
+        v = ldexp((double)(8 + m), e - 10); /* (1 + m/8) * 2^(e-7) */
+    return sign ? -v : v;
+}
+
+/* ---------------------------------------------------------------- decode -- */
+
+/* Error codes (negative): */
+#define ORACLE_EINVAL (-1)  /* bad shape or argument */
+#define ORACLE_ELEN   (-2)  /* a length outside [0, pt_stride * P] */
+#define ORACLE_EPAGE  (-3)  /* a used page id outside [0, num_pages) */
+
+/*
+ * Decode attention for the requests listed in req_ids (n_req entries; NULL
+ * means all B requests in order). Host pointers:
+ *   q          [B][Hq][D] bf16 bits
+ *   k_cache    [num_pages][Hkv][P][D] bf16 bits (kv_fp8 = 0) or e4m3fn codes
+ *   v_cache    same layout as k_cache
+ *   k_scale, v_scale [B][Hkv] fp32 (fp8 only; ignored for bf16)
+ *   page_table [B][pt_stride] int32, lengths [B] int32
+ *   out        [n_req][Hq][D] fp64, lse [n_req][Hq] fp64
+ * threads <= 0 uses the OpenMP default.
+ */
+int oracle_decode(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
+                  int32_t num_pages, int32_t pt_stride, int32_t kv_fp8,
+                  const uint16_t *q, const void *k_cache, const void *v_cache,
+                  const float *k_scale, const float *v_scale,
+                  const int32_t *page_table, const int32_t *lengths, double sm_scale,
+                  const int32_t *req_ids, int32_t n_req, double *out, double *lse,
+                  int32_t threads)
+{
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || D <= 0 || P <= 0 || pt_stride < 0 ||
+        num_pages < 0 || !out || !lse || (kv_fp8 && (!k_scale || !v_scale)))
+        return ORACLE_EINVAL;
+    if (!req_ids)
+        n_req = B;
+    const int32_t G = Hq / Hkv;
+
+    /* validate everything first, so no worker thread ever reads out of bounds */
+    for (int32_t i = 0; i < n_req; ++i) {
+        int32_t b = req_ids ? req_ids[i] : i;
+        if (b < 0 || b >= B)
+            return ORACLE_EINVAL;
+        int64_t L = lengths[b];
+        if (L < 0 || L > (int64_t)pt_stride * P)
+            return ORACLE_ELEN;
+        for (int64_t pg = 0; pg < (L + P - 1) / P; ++pg) {
+            int32_t id = page_table[(int64_t)b * pt_stride + pg];
+            if (id < 0 || id >= num_pages)
+                return ORACLE_EPAGE;
+        }
+    }
+
+    const int64_t n_items = (int64_t)n_req * Hkv;
+    int failed = 0;
+#ifdef _OPENMP
+    if (threads <= 0)
+        threads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(threads)
+#endif
+    for (int64_t item = 0; item < n_items; ++item) {
+        const int32_t i = (int32_t)(item / Hkv), g = (int32_t)(item % Hkv);
+        const int32_t b = req_ids ? req_ids[i] : i;
+        const int64_t L = lengths[b];
+        double *o = out + ((int64_t)i * Hq + (int64_t)g * G) * D;
+        double *ls = lse + (int64_t)i * Hq + (int64_t)g * G;
+        if (L == 0) {
+            memset(o, 0, sizeof(double) * (size_t)G * D);
+            for (int32_t hh = 0; hh < G; ++hh)
+                ls[hh] = -INFINITY;
+            continue;
+        }
+        double *qd = malloc(sizeof(double) * (size_t)G * D);
+        double *row = malloc(sizeof(double) * (size_t)D);
+        double *s = malloc(sizeof(double) * (size_t)L * G);
+        double *mx = malloc(sizeof(double) * (size_t)G);
+        double *sum = malloc(sizeof(double) * (size_t)G);
+        if (!qd || !row || !s || !mx || !sum) {
+            free(qd); free(row); free(s); free(mx); free(sum);
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            failed = 1;
+            continue;
+        }
+        for (int32_t hh = 0; hh < G; ++hh)
+            for (int32_t d = 0; d < D; ++d)
+                qd[(int64_t)hh * D + d] =
+                    oracle_bf16_to_f64(q[((int64_t)b * Hq + (int64_t)g * G + hh) * D + d]);
+        const double ksc = kv_fp8 ? (double)k_scale[(int64_t)b * Hkv + g] : 1.0;
+        const double vsc = kv_fp8 ? (double)v_scale[(int64_t)b * Hkv + g] : 1.0;
+
+        /* pass 1: scores */
+        for (int64_t j = 0; j < L; ++j) {
+            const int64_t page = page_table[(int64_t)b * pt_stride + j / P];
+            const int64_t off = ((page * Hkv + g) * P + j % P) * D;
+            for (int32_t d = 0; d < D; ++d)
+                row[d] = kv_fp8 ? oracle_e4m3fn_to_f64(((const uint8_t *)k_cache)[off + d]) * ksc
+                                : oracle_bf16_to_f64(((const uint16_t *)k_cache)[off + d]);
+            for (int32_t hh = 0; hh < G; ++hh) {
+                double acc = 0.0;
+                for (int32_t d = 0; d < D; ++d)
+                    acc += qd[(int64_t)hh * D + d] * row[d];
+                s[j * G + hh] = sm_scale * acc;
+            }
+        }
+        /* pass 2: max, then weights exp(s - m) and their sum */
+        for (int32_t hh = 0; hh < G; ++hh) {
+            double m = -INFINITY;
+            for (int64_t j = 0; j < L; ++j)
+                if (s[j * G + hh] > m)
+                    m = s[j * G + hh];
+            mx[hh] = m;
+            sum[hh] = 0.0;
+        }
+        for (int64_t j = 0; j < L; ++j)
+            for (int32_t hh = 0; hh < G; ++hh) {
+                s[j * G + hh] = exp(s[j * G + hh] - mx[hh]);
+                sum[hh] += s[j * G + hh];
+            }
+        /* pass 3: weighted sum of value rows */
+        memset(o, 0, sizeof(double) * (size_t)G * D);
+        for (int64_t j = 0; j < L; ++j) {
+            const int64_t page = page_table[(int64_t)b * pt_stride + j / P];
+            const int64_t off = ((page * Hkv + g) * P + j % P) * D;
+            for (int32_t d = 0; d < D; ++d)
+                row[d] = kv_fp8 ? oracle_e4m3fn_to_f64(((const uint8_t *)v_cache)[off + d]) * vsc
+                                : oracle_bf16_to_f64(((const uint16_t *)v_cache)[off + d]);
+            for (int32_t hh = 0; hh < G; ++hh) {
+                const double w = s[j * G + hh];
+                for (int32_t d = 0; d < D; ++d)
+                    o[(int64_t)hh * D + d] += w * row[d];
+            }
+        }
+        for (int32_t hh = 0; hh < G; ++hh) {
+            for (int32_t d = 0; d < D; ++d)
+                o[(int64_t)hh * D + d] /= sum[hh];
+            ls[hh] = mx[hh] + log(sum[hh]);
+        }
+        free(qd); free(row); free(s); free(mx); free(sum);
+    }
+    return failed ? ORACLE_EINVAL : 0;
+}
+
+/* ------------------------------------------------------------------ plan -- */
+
+/*
+ * Tile plan of one decode step (integer only, int64 internally).
+ *
+ * Units. Request b has n_b = ceil(Le_b / T) uniform tiles of T tokens (the last
+ * may be short), where Le_b = L_b if 0 <= L_b <= pt_stride*P, else 0 and status
+ * bit 1 is set. A unit is (b, g, t) with g < Hkv, t < n_b, numbered in the order
+ * b, then g, then t; N = Hkv * sum_b n_b units in all.
+ *
+ * Dynamic mode (mode 0). With W workgroups, W_eff = min(W, N). Workgroup w owns
+ * the contiguous unit range [floor(w*N/W_eff), floor((w+1)*N/W_eff)), so no two
+ * workgroups differ by more than one unit. Unit u's owner is
+ * floor(((u+1)*W_eff - 1) / N). A segment is a maximal run of one (b, g) inside
+ * one workgroup; pair bg = b*Hkv + g has segs(bg) = owner(last) - owner(first) + 1
+ * segments (0 if n_b = 0), and its segments take partial-result slots
+ * seg_prefix[bg] .. seg_prefix[bg+1]-1 in workgroup order; first_wg[bg] is the
+ * owner of its first unit (-1 if it has none). A pair with one segment is
+ * written directly; pairs with two or more are merged afterwards.
+ *
+ * Static mode (mode 1). S splits per pair (S > 0, given). Chunk C =
+ * ceil(maxLe / S) rounded up to a multiple of lcm(P, T) (0 if maxLe = 0);
+ * split s of pair bg covers tokens [s*C, min((s+1)*C, Le_b)) and may be empty.
+ * One workgroup per (b, g, s): N = W_eff = B*Hkv*S, seg_prefix[bg] = bg*S,
+ * first_wg[bg] = bg*S. wg_begin and wg_start_b are not written.
+ *
+ * Outputs (caller-allocated):
+ *   header[8]      = {status, N, W_eff, maxLe, C (static) or 0, S (static) or 0,
+ *                     sum_b n_b, T}
+ *   len_eff[B], tiles_prefix[B+1], seg_prefix[B*Hkv+1], first_wg[B*Hkv],
+ *   wg_begin[W+1]  (dynamic: floor(w*N/W_eff) for w <= W_eff, N beyond),
+ *   wg_start_b[W]  (dynamic: request of workgroup w's first unit; B if none).
+ * Returns 0, or ORACLE_EINVAL for bad arguments, or -4 if N exceeds INT32_MAX.
+ */
+static int64_t gcd64(int64_t a, int64_t b)
+{
+    while (b) {
+        int64_t t = a % b;
+        a = b;
+        b = t;
+    }
+    return a;
+}
+
+int oracle_plan(int32_t mode, int32_t B, int32_t Hkv, int32_t P, int32_t pt_stride,
+                int32_t T, int32_t W, int32_t S, const int32_t *lengths,
+                int32_t *header, int32_t *len_eff, int32_t *tiles_prefix,
+                int32_t *seg_prefix, int32_t *first_wg, int32_t *wg_begin,
+                int32_t *wg_start_b)
+{
+    if (B < 0 || Hkv <= 0 || P <= 0 || pt_stride < 0 || T <= 0 || W <= 0 ||
+        (mode != 0 && mode != 1) || (mode == 1 && S <= 0))
+        return ORACLE_EINVAL;
+    int32_t status = 0;
+    int64_t total = 0, maxle = 0;
+    tiles_prefix[0] = 0;
+    for (int32_t b = 0; b < B; ++b) {
+        int64_t L = lengths[b];
+        if (L < 0 || L > (int64_t)pt_stride * P) {
+            status |= 1;
+            L = 0;
+        }
+        len_eff[b] = (int32_t)L;
+        if (L > maxle)
+            maxle = L;
+        total += (L + T - 1) / T;
+        if (total > INT32_MAX)
+            return -4;
+        tiles_prefix[b + 1] = (int32_t)total;
+    }
+    if (mode == 1) {
+        const int64_t NB = (int64_t)B * Hkv * S;
+        if (NB > INT32_MAX)
+            return -4;
+        const int64_t gran = (int64_t)P / gcd64(P, T) * T;
+        int64_t C = 0;
+        if (maxle > 0) {
+            C = (maxle + S - 1) / S;
+            C = (C + gran - 1) / gran * gran;
+        }
+        for (int64_t bg = 0; bg < (int64_t)B * Hkv; ++bg) {
+            seg_prefix[bg] = (int32_t)(bg * S);
+            first_wg[bg] = (int32_t)(bg * S);
+        }
+        seg_prefix[(int64_t)B * Hkv] = (int32_t)NB;
+        const int32_t h[8] = {status, (int32_t)NB, (int32_t)NB, (int32_t)maxle,
+                              (int32_t)C, S, (int32_t)total, T};
+        memcpy(header, h, sizeof h);
+        return 0;
+    }
+    const int64_t N = total * Hkv;
+    if (N > INT32_MAX)
+        return -4;
+    const int64_t We = N < W ? N : W;
+    int64_t nseg = 0;
+    seg_prefix[0] = 0;
+    for (int32_t b = 0; b < B; ++b) {
+        const int64_t nb = tiles_prefix[b + 1] - tiles_prefix[b];
+        for (int32_t g = 0; g < Hkv; ++g) {
+            const int64_t bg = (int64_t)b * Hkv + g;
+            if (nb == 0) {
+                first_wg[bg] = -1;
+            } else {
+                const int64_t u0 = (int64_t)tiles_prefix[b] * Hkv + g * nb;
+                const int64_t u1 = u0 + nb - 1;
+                const int64_t w0 = ((u0 + 1) * We - 1) / N;
+                const int64_t w1 = ((u1 + 1) * We - 1) / N;
+                first_wg[bg] = (int32_t)w0;
+                nseg += w1 - w0 + 1;
+            }
+            seg_prefix[bg + 1] = (int32_t)nseg;
+        }
+    }
+    for (int64_t w = 0; w <= W; ++w)
+        wg_begin[w] = (int32_t)(w <= We && We > 0 ? w * N / We : N);
+    /* request of each workgroup's first unit: the b with
+       Hkv*tiles_prefix[b] <= u < Hkv*tiles_prefix[b+1] */
+    int32_t b = 0;
+    for (int64_t w = 0; w < W; ++w) {
+        if (w >= We) {
+            wg_start_b[w] = B;
+            continue;
+        }
+        const int64_t u = wg_begin[w];
+        while (b < B && (int64_t)tiles_prefix[b + 1] * Hkv <= u)
+            ++b;
+        wg_start_b[w] = b;
+    }
+    const int32_t h[8] = {status, (int32_t)N, (int32_t)We, (int32_t)maxle, 0, 0,
+                          (int32_t)total, T};
+    memcpy(header, h, sizeof h);
+    return 0;
+}

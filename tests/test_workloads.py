@@ -1,0 +1,54 @@
+"""The seeded input recipes (no GPU): determinism and realized sizes."""
+import numpy as np
+import torch
+
+from variable_length_kv_amd import workloads as wl
+
+
+def test_realized_lengths_at_seed_0():
+    sums = [int(wl.config_lengths(c).sum()) for c in range(5)]
+    assert sums == [1281, 284965, 79000, 512126, 1648574]
+    L3 = wl.config_lengths(3)
+    assert L3.min() >= 128 and L3.max() <= 131072
+    L1 = wl.config_lengths(1)
+    assert L1.min() >= 1000 and L1.max() <= 16000
+
+
+def test_trace_lengths_follow_the_rules():
+    L, ev = wl.trace_lengths()
+    assert L.shape == (256, 96)
+    for s in range(255):
+        grown = L[s] + 1
+        changed = {slot for slot, _ in ev[s]}
+        for b in range(96):
+            if b in changed:
+                assert 256 <= L[s + 1, b] <= 4096
+            else:
+                assert L[s + 1, b] == grown[b]
+
+
+def test_generation_is_deterministic_and_thread_count_free():
+    a = wl.normal_f32(5, (1,), 3 * wl.CHUNK + 17)
+    old = wl._workers
+    try:
+        wl._workers = lambda: 1
+        b = wl.normal_f32(5, (1,), 3 * wl.CHUNK + 17)
+    finally:
+        wl._workers = old
+    assert np.array_equal(a, b)
+    c1 = wl.make_case("x", [5, 40], Hq=4, Hkv=2, P=16, seed=3)
+    c2 = wl.make_case("x", [5, 40], Hq=4, Hkv=2, P=16, seed=3)
+    assert torch.equal(c1.k_cache, c2.k_cache) and np.array_equal(c1.page_table, c2.page_table)
+
+
+def test_page_table_is_a_permutation():
+    c = wl.config_case(0)
+    used = np.concatenate([c.page_table[b, :-(-int(L) // c.P)] for b, L in enumerate(c.lengths)])
+    assert sorted(used.tolist()) == list(range(c.num_pages))
+
+
+def test_fp8_codes_saturate_and_scale():
+    c = wl.make_case("x", [20, 1], Hq=4, Hkv=2, P=16, kv_dtype="fp8", seed=4)
+    k = c.k_cache.view(torch.float8_e4m3fn).float()
+    assert torch.isfinite(k).all() and k.abs().max() <= 448
+    assert c.k_scale.shape == (2, 2) and (c.k_scale > 0).all()
