@@ -1,0 +1,193 @@
+/*
+ * vlkv_attn.h — C ABI of the MI355X (gfx950) variable-length paged decode
+ * attention library (libvlkv_attn.so).
+ *
+ * The operation. One decode step of attention serving many requests whose
+ * context lengths differ widely: each request b has one query per query head and
+ * attends to its L_b cached key/value rows. The source article motivates it with
+ * a batch where one request carries 16,000 tokens of context and another has
+ * just started at 1,000: under a static schedule one GPU block gets far more
+ * work than the rest and the longest task decides when the launch ends. Its
+ * "Dynamic Attention" cuts the KV-cache work into uniform tiles, hands them to
+ * workgroups according to the current load, and rebuilds that mapping as
+ * lengths change during decode; its baseline is a static split-k
+ * [Tencent HPC lands in SGLang, challenging default inference kernels, sec.
+ * "Why Tencent HPC matters for online model serving"]. Cache precision is one
+ * of the benchmark dimensions it lists [same page, sec. "What the 48.8% TPOT
+ * claim does not prove"], hence the fp8 cache option.
+ *
+ * Per step the caller enqueues, on one stream and with one workspace:
+ *     attn_plan  -> attn_decode -> attn_combine
+ * The result is, for request b and query head h (kv head g = h / (Hq/Hkv)):
+ *     o[b][h] = sum_j softmax_j(sm_scale * q[b][h] . K_j) V_j,
+ *     lse[b][h] = ln sum_j exp(sm_scale * q[b][h] . K_j)
+ * over j = 0..L_b-1, with K_j = k_cache[page_table[b][j/P]][g][j%P][:].
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked (device) are HIP device memory on the current device;
+ *     (host) pointers are ordinary host memory read before the call returns.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued and
+ *     never waited for, except by attn_get_status.
+ *   - The caller allocates and owns every buffer. The library allocates no
+ *     memory, keeps no pointer after a call returns and has no global mutable
+ *     state; calls on different workspaces may run concurrently.
+ *   - Return value: ATTN_OK, or an ATTN_ERR_* code. Argument and shape checks
+ *     happen on the host before anything is enqueued; on error nothing is
+ *     enqueued and attn_last_error() describes the problem.
+ *   - Data errors that only the device can see (a length beyond the page
+ *     table, a page id outside [0, num_pages)) set bits in a status word inside
+ *     the workspace; the affected rows are skipped, never read out of bounds.
+ */
+#ifndef VLKV_ATTN_H
+#define VLKV_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* return codes */
+#define ATTN_OK               0
+#define ATTN_ERR_INVALID_ARG  1  /* null pointer, bad shape, workspace too small */
+#define ATTN_ERR_UNSUPPORTED  2  /* a shape or dtype this build does not implement */
+#define ATTN_ERR_HIP          3  /* a HIP runtime call or kernel launch failed */
+
+/* kv_dtype */
+#define ATTN_KV_BF16      0      /* bfloat16 K/V rows */
+#define ATTN_KV_FP8_E4M3  1      /* OCP e4m3fn codes, fp32 scale per (request, kv head) */
+
+/* mode */
+#define ATTN_DYNAMIC  0          /* balanced per-step tile plan */
+#define ATTN_STATIC   1          /* static split-K: S fixed splits per (request, kv head) */
+
+/* status word bits (attn_get_status) */
+#define ATTN_STATUS_BAD_LENGTH  1u  /* some L_b < 0 or L_b > pt_stride * page_size: treated as 0 */
+#define ATTN_STATUS_BAD_PAGE    2u  /* some used page id outside [0, num_pages): its rows skipped */
+
+/*
+ * Problem shape (host struct, read during the call).
+ *   batch          B, number of requests (>= 1)
+ *   num_q_heads    Hq;  num_kv_heads Hkv; Hq % Hkv == 0 and 1 <= Hq/Hkv <= 16
+ *   head_dim       D; this build supports 128
+ *   page_size      P tokens per page; a multiple of 16
+ *   num_pages      physical pages in each cache
+ *   pt_stride      row length of the page table (max pages per request)
+ *   tile_tokens    T, the uniform tile; a multiple of 64
+ *   num_wgs        W, workgroups of the dynamic decode launch (>= 1); a good
+ *                  value is 2 per compute unit (attn_device_cu_count)
+ *   kv_dtype       ATTN_KV_BF16 or ATTN_KV_FP8_E4M3
+ *   mode           ATTN_DYNAMIC or ATTN_STATIC
+ *   static_splits  S for ATTN_STATIC (>= 1); 0 picks
+ *                  clamp(ceil(num_wgs / (B*Hkv)), 1, ceil(pt_stride*P / T))
+ */
+typedef struct attn_shape {
+    int32_t batch;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t page_size;
+    int32_t num_pages;
+    int32_t pt_stride;
+    int32_t tile_tokens;
+    int32_t num_wgs;
+    int32_t kv_dtype;
+    int32_t mode;
+    int32_t static_splits;
+} attn_shape;
+
+/*
+ * Validate a shape without touching the GPU. Returns ATTN_OK,
+ * ATTN_ERR_INVALID_ARG or ATTN_ERR_UNSUPPORTED (see attn_last_error()).
+ */
+int attn_check_shape(const attn_shape *shape);
+
+/*
+ * Bytes of workspace the three calls need for this shape, for any lengths
+ * within pt_stride * page_size. Host only, pure. Returns 0 for an invalid
+ * shape. The workspace must be device memory aligned to 256 bytes.
+ */
+size_t attn_workspace_bytes(const attn_shape *shape);
+
+/* Effective number of static splits S for this shape (ATTN_STATIC), or 0. */
+int32_t attn_static_splits(const attn_shape *shape);
+
+/*
+ * Number of compute units of HIP device `device` in *cus (host pointer).
+ * Returns ATTN_OK or ATTN_ERR_HIP.
+ */
+int attn_device_cu_count(int device, int32_t *cus);
+
+/*
+ * Build the tile plan for this step into the workspace (one small kernel).
+ *   lengths    (device) int32 [B], current context length of each request
+ *   page_table (device) int32 [B][pt_stride]; not read by the planner
+ *   workspace  (device) >= attn_workspace_bytes(shape) bytes, 256-B aligned
+ * Dynamic mode: the (request, kv head, tile) units are numbered request-major
+ * and cut into num_wgs contiguous, equal (+-1) ranges; each maximal run of one
+ * (request, kv head) inside a range is a segment with its own partial slot.
+ * Static mode: chunk = ceil(max L / S) rounded up to a multiple of
+ * lcm(page_size, tile_tokens); split s of each (request, kv head) covers
+ * tokens [s*chunk, min((s+1)*chunk, L_b)) and may be empty.
+ * The workspace contents stay valid until the next attn_plan on it.
+ */
+int attn_plan(const attn_shape *shape, const int32_t *lengths, const int32_t *page_table,
+              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Decode attention over the plan in `workspace` (same stream).
+ *   q          (device) bf16 [B][Hq][D]
+ *   k_cache    (device) [num_pages][Hkv][P][D], bf16 or uint8 e4m3fn codes
+ *   v_cache    (device) same layout and dtype as k_cache
+ *   k_scale    (device) fp32 [B][Hkv] for ATTN_KV_FP8_E4M3, else NULL
+ *   v_scale    (device) fp32 [B][Hkv] for ATTN_KV_FP8_E4M3, else NULL
+ *   page_table (device) int32 [B][pt_stride]: page of tokens [i*P, (i+1)*P)
+ * The lengths are the validated copy attn_plan stored in the workspace.
+ *   sm_scale   softmax scale applied to q . k (e.g. 1/sqrt(D))
+ *   out        (device) bf16 [B][Hq][D]; (request, kv head) pairs handled by
+ *              a single workgroup are written here directly
+ *   lse        (device) fp32 [B][Hq] natural-log log-sum-exp, or NULL
+ * Rows j >= L_b of a request's last page are never used. K/V, q, scales and
+ * the page table are only read.
+ */
+int attn_decode(const attn_shape *shape, const void *q, const void *k_cache,
+                const void *v_cache, const float *k_scale, const float *v_scale,
+                const int32_t *page_table, float sm_scale, void *workspace,
+                size_t workspace_bytes, void *out, float *lse, void *stream);
+
+/*
+ * Merge the partial results of (request, kv head) pairs that were split over
+ * several workgroups (log-sum-exp weighting), and write o = 0, lse = -inf for
+ * requests with L_b = 0. Must follow attn_decode on the same stream and
+ * workspace. out, lse as in attn_decode.
+ */
+int attn_combine(const attn_shape *shape, const void *workspace, size_t workspace_bytes,
+                 void *out, float *lse, void *stream);
+
+/*
+ * Copy the status word of the last plan/decode on this workspace into *flags
+ * (host pointer). SYNCHRONISES `stream`; meant for tests and debugging, not
+ * for the per-step path.
+ */
+int attn_get_status(const void *workspace, uint32_t *flags, void *stream);
+
+/*
+ * Copy the plan arrays out of the workspace into host memory (synchronises
+ * `stream`), for checking the device planner against a CPU planner. Each host
+ * pointer may be NULL to skip that array. Sizes: header[8], len_eff[B],
+ * tiles_prefix[B+1], seg_prefix[B*Hkv+1], first_wg[B*Hkv], wg_begin[W+1],
+ * wg_start_b[W]. header = {status, N, W_eff, max L, chunk, S, total tiles, T}.
+ */
+int attn_read_plan(const attn_shape *shape, const void *workspace, int32_t *header,
+                   int32_t *len_eff, int32_t *tiles_prefix, int32_t *seg_prefix,
+                   int32_t *first_wg, int32_t *wg_begin, int32_t *wg_start_b, void *stream);
+
+/* Text of the last error on the calling thread ("" if none). */
+const char *attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VLKV_ATTN_H */

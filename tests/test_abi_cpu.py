@@ -1,0 +1,102 @@
+"""The C ABI library without a GPU: it loads, exports every declared entry
+point, and rejects bad shapes and arguments on the host before any launch."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from variable_length_kv_amd import lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names |= set(re.findall(r"\b(attn_[a-z_0-9]+)\s*\(", src))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(L.LIB_PATH)
+    declared = _declared()
+    assert declared, "no declarations found"
+    assert declared == set(L.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def _shape(**kw):
+    base = dict(batch=4, num_q_heads=8, num_kv_heads=1, page_size=16, num_pages=100, pt_stride=63,
+                num_wgs=512)
+    base.update(kw)
+    return L.AttnShape(**base)
+
+
+def test_valid_shape_and_workspace_size():
+    s = _shape()
+    L.attn_check_shape(s)
+    n = L.attn_workspace_bytes(s)
+    # header + plan arrays + partial slots (B*Hkv + W) * G * (D + 1) floats
+    assert n >= (4 + 512) * 8 * 129 * 4
+    st = _shape(mode=L.ATTN_STATIC, static_splits=3)
+    assert L.attn_static_splits(st) == 3
+    assert L.attn_workspace_bytes(st) >= 4 * 3 * 8 * 129 * 4
+
+
+def test_default_static_splits():
+    # ceil(W / (B*Hkv)) clamped to [1, ceil(pt_stride*P / T)]
+    assert L.attn_static_splits(_shape(mode=L.ATTN_STATIC, num_wgs=512, batch=64, num_kv_heads=8)) == 1
+    assert L.attn_static_splits(_shape(mode=L.ATTN_STATIC, num_wgs=512, batch=4, num_kv_heads=1)) == 16
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), L.ATTN_ERR_INVALID_ARG),
+    (dict(num_q_heads=6, num_kv_heads=4), L.ATTN_ERR_INVALID_ARG),
+    (dict(num_q_heads=64, num_kv_heads=2), L.ATTN_ERR_UNSUPPORTED),
+    (dict(head_dim=64), L.ATTN_ERR_UNSUPPORTED),
+    (dict(page_size=8), L.ATTN_ERR_INVALID_ARG),
+    (dict(page_size=24), L.ATTN_ERR_INVALID_ARG),
+    (dict(tile_tokens=32), L.ATTN_ERR_UNSUPPORTED),
+    (dict(num_wgs=0), L.ATTN_ERR_INVALID_ARG),
+    (dict(kv_dtype=7), L.ATTN_ERR_UNSUPPORTED),
+    (dict(mode=3), L.ATTN_ERR_INVALID_ARG),
+    (dict(num_pages=0), L.ATTN_ERR_INVALID_ARG),
+    (dict(pt_stride=0), L.ATTN_ERR_INVALID_ARG),
+])
+def test_bad_shapes_are_rejected(kw, code):
+    s = _shape(**kw)
+    with pytest.raises(L.AttnError) as e:
+        L.attn_check_shape(s)
+    assert e.value.code == code
+    assert L.load().attn_workspace_bytes(ctypes.byref(s.c())) == 0
+
+
+def test_null_arguments_rejected_before_launch():
+    lib = L.load()
+    s = _shape().c()
+    ws = ctypes.c_void_p(256)  # never dereferenced: rejected first
+    assert lib.attn_plan(ctypes.byref(s), None, None, ws, 1 << 30, None) == L.ATTN_ERR_INVALID_ARG
+    assert b"lengths" in lib.attn_last_error()
+    assert lib.attn_plan(ctypes.byref(s), ctypes.c_void_p(16), None, None, 1 << 30, None) == L.ATTN_ERR_INVALID_ARG
+    assert lib.attn_plan(ctypes.byref(s), ctypes.c_void_p(16), None, ctypes.c_void_p(300), 1 << 30, None) \
+        == L.ATTN_ERR_INVALID_ARG  # misaligned workspace
+    assert lib.attn_plan(ctypes.byref(s), ctypes.c_void_p(16), None, ws, 16, None) == L.ATTN_ERR_INVALID_ARG
+    assert b"workspace" in lib.attn_last_error()
+    args = [ctypes.byref(s), None, ctypes.c_void_p(16), ctypes.c_void_p(16), None, None, ctypes.c_void_p(16),
+            ctypes.c_float(0.1), ws, ctypes.c_size_t(1 << 30), ctypes.c_void_p(16), None, None]
+    assert lib.attn_decode(*args) == L.ATTN_ERR_INVALID_ARG
+    args[7] = ctypes.c_float(float("nan"))
+    args[1] = ctypes.c_void_p(16)
+    assert lib.attn_decode(*args) == L.ATTN_ERR_INVALID_ARG
+    s8 = _shape(kv_dtype=L.ATTN_KV_FP8_E4M3).c()
+    args = [ctypes.byref(s8), ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16), None, None,
+            ctypes.c_void_p(16), ctypes.c_float(0.1), ws, ctypes.c_size_t(1 << 30), ctypes.c_void_p(16), None, None]
+    assert lib.attn_decode(*args) == L.ATTN_ERR_INVALID_ARG
+    assert b"scale" in lib.attn_last_error()
+    assert lib.attn_combine(ctypes.byref(s), ws, ctypes.c_size_t(1 << 30), None, None, None) == L.ATTN_ERR_INVALID_ARG
+    assert lib.attn_get_status(None, None, None) == L.ATTN_ERR_INVALID_ARG

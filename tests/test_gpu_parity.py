@@ -1,0 +1,218 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU reference.
+
+Tolerances: |o_gpu - o_ref| <= 1e-2 + 1e-2 |o_ref| for bf16 caches and
+5e-2 + 5e-2 |o_ref| for fp8 caches, elementwise; lse within 1e-3; and, since
+outputs shrink with context length, a per-(request, head) relative L2 error of
+at most 2e-2 (bf16) / 6e-2 (fp8) so that a dropped tile cannot hide under the
+absolute tolerance. Cache rows past each request's length are NaN-poisoned.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from variable_length_kv_amd import lib as L
+from variable_length_kv_amd import workloads as wl
+
+from gpu_helpers import (BF16_TOL, FP8_TOL, check_against_oracle, check_close, device_inputs, num_cus, run,
+                         shape_for)
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(lengths, **kw):
+    kw.setdefault("Hq", 8)
+    kw.setdefault("Hkv", 1)
+    kw.setdefault("P", 16)
+    return wl.make_case("t", lengths, **kw)
+
+
+def test_tiny_workload_all_outputs():
+    c = wl.config_case(0)
+    out, lse, att = run(c)
+    check_against_oracle(c, out, lse, what="tiny")
+    assert att.status() == 0
+
+
+@pytest.mark.parametrize("W", [1, 2, 3, 7, 64, 1000])
+def test_tiny_workload_any_workgroup_count(W):
+    c = wl.config_case(0)
+    out, lse, _ = run(c, W=W)
+    check_against_oracle(c, out, lse, what=f"W={W}")
+
+
+@pytest.mark.parametrize("T", [64, 128, 256])
+def test_tile_sizes(T):
+    c = _case([1, 63, 64, 65, 300, 513], Hq=16, Hkv=2, P=32, seed=1)
+    out, lse, _ = run(c, T=T, W=9)
+    check_against_oracle(c, out, lse, what=f"T={T}")
+
+
+@pytest.mark.parametrize("L1", [1, 2, 15, 16, 17, 31, 33, 47, 63, 64, 65, 127, 128, 129, 1023, 1024, 1025])
+def test_boundary_lengths_single_request(L1):
+    c = _case([L1], Hq=8, Hkv=1, P=16, seed=2)
+    for W in (1, 5):
+        out, lse, _ = run(c, W=W)
+        check_against_oracle(c, out, lse, what=f"L={L1} W={W}")
+
+
+@pytest.mark.parametrize("hq,hkv", [(1, 1), (8, 8), (16, 1), (12, 4), (64, 8)])
+def test_head_groupings(hq, hkv):
+    c = _case([5, 70, 200], Hq=hq, Hkv=hkv, P=64, seed=3)
+    out, lse, _ = run(c, W=11)
+    check_against_oracle(c, out, lse, what=f"Hq={hq} Hkv={hkv}")
+
+
+def test_random_batches_dynamic():
+    rng = np.random.default_rng(7)
+    for it in range(6):
+        B = int(rng.integers(1, 24))
+        P = int(rng.choice([16, 32, 64]))
+        lengths = rng.integers(0, 700, B)
+        lengths[int(rng.integers(B))] = int(rng.integers(1, 3000))
+        c = _case(lengths, Hq=8, Hkv=2, P=P, seed=10 + it)
+        W = int(rng.choice([1, 4, 13, 100, 512]))
+        out, lse, _ = run(c, W=W)
+        check_against_oracle(c, out, lse, what=f"random it={it} W={W}")
+
+
+@pytest.mark.parametrize("S", [0, 1, 2, 3, 8, 40])
+def test_static_split_k(S):
+    c = _case([16000 // 16, 1000 // 16, 1, 0, 333], Hq=8, Hkv=2, P=16, seed=4)
+    out, lse, att = run(c, mode=L.ATTN_STATIC, S=S, W=16)
+    check_against_oracle(c, out, lse, what=f"static S={S}")
+
+
+def test_empty_requests():
+    c = _case([0, 17, 0, 0, 40], Hq=8, Hkv=2, P=16, seed=5)
+    for mode in (L.ATTN_DYNAMIC, L.ATTN_STATIC):
+        out, lse, _ = run(c, mode=mode, W=3)
+        assert np.all(out[[0, 2, 3]] == 0) and np.all(lse[[0, 2, 3]] == -np.inf)
+        check_against_oracle(c, out, lse, what=f"empties mode={mode}")
+    c0 = _case([0, 0], Hq=8, Hkv=1, P=16, seed=6)
+    out, lse, _ = run(c0, W=4)
+    assert np.all(out == 0) and np.all(lse == -np.inf)
+
+
+def test_single_token_returns_v_bitwise():
+    c = _case([1, 1, 1, 1], Hq=16, Hkv=2, P=16, seed=7)
+    out, _, _ = run(c, W=2)
+    for b in range(4):
+        for h in range(16):
+            page = int(c.page_table[b, 0])
+            v = c.v_cache[page, h // 8, 0].double().numpy()
+            assert np.array_equal(out[b, h], v)
+
+
+def test_identical_value_rows():
+    c = _case([37, 300, 1500], Hq=8, Hkv=1, P=16, seed=8)
+    row = c.v_cache[0, 0, 0].clone()
+    c.v_cache[:] = row
+    out, _, _ = run(c, W=7)
+    r = row.double().numpy()
+    ulp = np.abs(r) * 2.0 ** -7 + 1e-30
+    assert np.all(np.abs(out - r[None, None, :]) <= ulp[None, None, :])
+
+
+def test_page_permutation_invariance_bitwise():
+    c = _case([30, 64, 129, 700], Hq=8, Hkv=2, P=16, seed=9)
+    out1, lse1, _ = run(c, W=5)
+    perm = np.random.default_rng(1).permutation(c.num_pages)
+    inv = torch.from_numpy(np.argsort(perm).astype(np.int64))
+    c2 = wl.Case(c.name, c.B, c.Hq, c.Hkv, c.D, c.P, c.lengths,
+                 np.where(c.page_table >= 0, perm[np.maximum(c.page_table, 0)], -1).astype(np.int32),
+                 c.num_pages, c.kv_dtype, c.q, c.k_cache[inv], c.v_cache[inv], None, None, c.sm_scale)
+    out2, lse2, _ = run(c2, W=5)
+    assert np.array_equal(out1, out2) and np.array_equal(lse1, lse2)
+
+
+def test_run_to_run_determinism():
+    c = _case([1000, 3, 250, 4000], Hq=16, Hkv=2, P=32, seed=10)
+    t = device_inputs(c)
+    a = run(c, t=t, W=37)
+    b = run(c, t=t, W=37)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_prefix_shared_pages():
+    """Two requests whose page tables alias the same physical prefix pages give
+    the same result as with a deep copy of those pages."""
+    c = _case([100, 130], Hq=8, Hkv=1, P=16, seed=11)
+    pt = c.page_table.copy()
+    pt[1, :4] = pt[0, :4]          # request 1 shares request 0's first 64 tokens
+    shared = wl.Case(c.name, c.B, c.Hq, c.Hkv, c.D, c.P, c.lengths, pt, c.num_pages, "bf16", c.q,
+                     c.k_cache, c.v_cache, None, None, c.sm_scale)
+    out, lse, _ = run(shared, W=3)
+    check_against_oracle(shared, out, lse, what="shared prefix")
+    # deep copy: copy the shared pages to fresh page ids
+    extra = torch.arange(c.num_pages, c.num_pages + 4)
+    k2 = torch.cat([c.k_cache, c.k_cache[torch.from_numpy(pt[0, :4].astype(np.int64))]])
+    v2 = torch.cat([c.v_cache, c.v_cache[torch.from_numpy(pt[0, :4].astype(np.int64))]])
+    pt2 = pt.copy()
+    pt2[1, :4] = extra.numpy()
+    copied = wl.Case(c.name, c.B, c.Hq, c.Hkv, c.D, c.P, c.lengths, pt2, c.num_pages + 4, "bf16", c.q,
+                     k2, v2, None, None, c.sm_scale)
+    out2, lse2, _ = run(copied, W=3)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+
+
+def test_bad_page_id_sets_status_and_stays_in_bounds():
+    c = _case([40, 40], Hq=8, Hkv=1, P=16, seed=12)
+    t = device_inputs(c)
+    t["pt"][1, 1] = c.num_pages + 5      # out of range: the kernel must skip it
+    out, lse, att = run(c, t=t, W=4)
+    assert att.status() & L.ATTN_STATUS_BAD_PAGE
+    check_against_oracle(c, out, lse, req_ids=[0], what="untouched request")
+
+
+def test_bad_length_sets_status():
+    c = _case([40, 40], Hq=8, Hkv=1, P=16, seed=13)
+    t = device_inputs(c)
+    t["len"][1] = 10 ** 6
+    out, lse, att = run(c, t=t, W=4)
+    assert att.status() & L.ATTN_STATUS_BAD_LENGTH
+    assert np.all(out[1] == 0) and np.all(lse[1] == -np.inf)
+    check_against_oracle(c, out, lse, req_ids=[0], what="valid request")
+
+
+# ------------------------------------------------------------------ fp8 --
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_fp8_cache(seed):
+    c = _case([1, 17, 64, 200, 1000, 0], Hq=16, Hkv=2, P=16, kv_dtype="fp8", seed=20 + seed)
+    for mode, W in ((L.ATTN_DYNAMIC, 7), (L.ATTN_DYNAMIC, 512), (L.ATTN_STATIC, 8)):
+        out, lse, _ = run(c, mode=mode, W=W)
+        check_against_oracle(c, out, lse, what=f"fp8 mode={mode} W={W}")
+
+
+def test_fp8_single_token_and_scale_algebra():
+    c = _case([1, 3], Hq=8, Hkv=1, P=16, kv_dtype="fp8", seed=22)
+    out, _, _ = run(c, W=2)
+    code = c.v_cache[int(c.page_table[0, 0]), 0, 0]
+    v = code.view(torch.float8_e4m3fn).float() * c.v_scale[0, 0].float()   # fp32 product, as the kernel
+    assert np.array_equal(out[0, 0], v.to(torch.bfloat16).double().numpy())
+    c2 = wl.Case(c.name, c.B, c.Hq, c.Hkv, c.D, c.P, c.lengths, c.page_table, c.num_pages, "fp8", c.q,
+                 c.k_cache, c.v_cache, c.k_scale, c.v_scale * 2, c.sm_scale)
+    out2, _, _ = run(c2, W=2)
+    assert np.array_equal(out2, 2 * out)
+
+
+# ------------------------------------------------------ full-size workloads --
+
+def _sample(lengths, n=6):
+    L_ = np.asarray(lengths)
+    idx = {int(np.argmax(L_)), int(np.argmin(L_)), 0, len(L_) - 1}
+    rng = np.random.default_rng(0)
+    idx |= set(rng.choice(len(L_), size=min(n, len(L_)), replace=False).tolist())
+    return sorted(idx)
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3])
+def test_full_size_workloads_sampled(cid):
+    c = wl.config_case(cid)
+    t = device_inputs(c)
+    for mode in (L.ATTN_DYNAMIC, L.ATTN_STATIC):
+        out, lse, att = run(c, mode=mode, t=t)
+        assert att.status() == 0
+        assert np.isfinite(out).all()
+        check_against_oracle(c, out, lse, req_ids=_sample(c.lengths), what=f"c{cid} mode={mode}")

@@ -1,0 +1,373 @@
+// C ABI of libvlkv_attn.so (declared in include/vlkv_attn.h): host-side
+// argument checks, the workspace layout, and the three per-step launches.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/vlkv_attn.h"
+#include "vlkv_internal.hpp"
+
+namespace vlkv {
+
+static thread_local std::string g_last_error;
+
+static int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+static int fail(int code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+static int ok()
+{
+    g_last_error.clear();
+    return ATTN_OK;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+static int32_t effective_splits(const attn_shape *s)
+{
+    if (s->static_splits > 0)
+        return s->static_splits;
+    const int64_t pairs = (int64_t)s->batch * s->num_kv_heads;
+    int64_t S = ceil_div(s->num_wgs, pairs);
+    const int64_t cap = ceil_div((int64_t)s->pt_stride * s->page_size, s->tile_tokens);
+    if (S > cap)
+        S = cap;
+    if (S < 1)
+        S = 1;
+    return (int32_t)S;
+}
+
+// Full shape validation. Returns ATTN_OK or an error code (with message).
+static int check(const attn_shape *s, Shape *out)
+{
+    if (!s)
+        return fail(ATTN_ERR_INVALID_ARG, "shape is NULL");
+    if (s->batch < 1 || s->batch > kMaxBatch)
+        return fail(ATTN_ERR_INVALID_ARG, "batch %d outside [1, %d]", s->batch, kMaxBatch);
+    if (s->num_q_heads < 1 || s->num_kv_heads < 1 || s->num_q_heads % s->num_kv_heads)
+        return fail(ATTN_ERR_INVALID_ARG, "num_q_heads %d must be a positive multiple of num_kv_heads %d",
+                    s->num_q_heads, s->num_kv_heads);
+    const int G = s->num_q_heads / s->num_kv_heads;
+    if (G > kMaxGroup)
+        return fail(ATTN_ERR_UNSUPPORTED, "query heads per kv head %d > %d", G, kMaxGroup);
+    if (s->head_dim != kHeadDim)
+        return fail(ATTN_ERR_UNSUPPORTED, "head_dim %d (only %d is built)", s->head_dim, kHeadDim);
+    if (s->page_size < 16 || s->page_size % 16)
+        return fail(ATTN_ERR_INVALID_ARG, "page_size %d must be a positive multiple of 16", s->page_size);
+    if (s->num_pages < 1)
+        return fail(ATTN_ERR_INVALID_ARG, "num_pages %d < 1", s->num_pages);
+    if (s->pt_stride < 1)
+        return fail(ATTN_ERR_INVALID_ARG, "pt_stride %d < 1", s->pt_stride);
+    if (s->tile_tokens < kBlockTokens || s->tile_tokens % kBlockTokens)
+        return fail(ATTN_ERR_UNSUPPORTED, "tile_tokens %d must be a positive multiple of %d",
+                    s->tile_tokens, kBlockTokens);
+    if (s->num_wgs < 1 || s->num_wgs > (1 << 20))
+        return fail(ATTN_ERR_INVALID_ARG, "num_wgs %d outside [1, 2^20]", s->num_wgs);
+    if (s->kv_dtype != ATTN_KV_BF16 && s->kv_dtype != ATTN_KV_FP8_E4M3)
+        return fail(ATTN_ERR_UNSUPPORTED, "kv_dtype %d", s->kv_dtype);
+    if (s->mode != ATTN_DYNAMIC && s->mode != ATTN_STATIC)
+        return fail(ATTN_ERR_INVALID_ARG, "mode %d", s->mode);
+    if (s->static_splits < 0)
+        return fail(ATTN_ERR_INVALID_ARG, "static_splits %d < 0", s->static_splits);
+    // every index the kernels form must fit its type
+    const int64_t max_tokens = (int64_t)s->pt_stride * s->page_size;
+    if (max_tokens > INT32_MAX / 2)
+        return fail(ATTN_ERR_INVALID_ARG, "pt_stride * page_size too large");
+    const int64_t max_units = (int64_t)s->batch * s->num_kv_heads * ceil_div(max_tokens, s->tile_tokens);
+    if (max_units > INT32_MAX / 2)
+        return fail(ATTN_ERR_INVALID_ARG, "batch * kv heads * tiles per request too large");
+    const int32_t S = s->mode == ATTN_STATIC ? effective_splits(s) : 0;
+    if (s->mode == ATTN_STATIC && (int64_t)s->batch * s->num_kv_heads * S > INT32_MAX / 2)
+        return fail(ATTN_ERR_INVALID_ARG, "batch * kv heads * splits too large");
+    if (s->mode == ATTN_STATIC && (int64_t)S * max_tokens > ((int64_t)INT32_MAX) * 4)
+        return fail(ATTN_ERR_INVALID_ARG, "static splits too large");
+    if (out) {
+        *out = Shape{s->batch, s->num_q_heads, s->num_kv_heads, G, s->head_dim, s->page_size,
+                     s->num_pages, s->pt_stride, s->tile_tokens, s->num_wgs,
+                     s->kv_dtype == ATTN_KV_FP8_E4M3, s->mode, S};
+    }
+    return ATTN_OK;
+}
+
+WsLayout ws_layout(const Shape &s)
+{
+    WsLayout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align256(off + bytes);
+        return at;
+    };
+    const int64_t nbg = (int64_t)s.B * s.Hkv;
+    L.max_slots = s.mode == ATTN_STATIC ? nbg * s.S : nbg + s.W;
+    L.header = take(sizeof(int32_t) * kHeaderInts);
+    L.len_eff = take(sizeof(int32_t) * s.B);
+    L.tiles_prefix = take(sizeof(int32_t) * (s.B + 1));
+    L.seg_prefix = take(sizeof(int32_t) * (nbg + 1));
+    L.first_wg = take(sizeof(int32_t) * nbg);
+    L.wg_begin = take(sizeof(int32_t) * (s.W + 1));
+    L.wg_start_b = take(sizeof(int32_t) * s.W);
+    L.part_lse = take(sizeof(float) * L.max_slots * s.G);
+    L.part_o = take(sizeof(float) * L.max_slots * s.G * s.D);
+    L.total = off;
+    return L;
+}
+
+template <typename T>
+static T *at(void *ws, size_t off)
+{
+    return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
+}
+template <typename T>
+static const T *at(const void *ws, size_t off)
+{
+    return reinterpret_cast<const T *>(static_cast<const char *>(ws) + off);
+}
+
+static int check_ws(const Shape &s, const void *ws, size_t bytes, WsLayout *L)
+{
+    *L = ws_layout(s);
+    if (!ws)
+        return fail(ATTN_ERR_INVALID_ARG, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(ws) % 256)
+        return fail(ATTN_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+    if (bytes < L->total)
+        return fail(ATTN_ERR_INVALID_ARG, "workspace %zu bytes < %zu needed", bytes, L->total);
+    return ATTN_OK;
+}
+
+static int hip_fail(hipError_t e, const char *what)
+{
+    return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace vlkv
+
+using namespace vlkv;
+
+extern "C" {
+
+int attn_check_shape(const attn_shape *shape)
+{
+    const int rc = check(shape, nullptr);
+    return rc == ATTN_OK ? ok() : rc;
+}
+
+size_t attn_workspace_bytes(const attn_shape *shape)
+{
+    Shape s;
+    if (check(shape, &s) != ATTN_OK)
+        return 0;
+    return ws_layout(s).total;
+}
+
+int32_t attn_static_splits(const attn_shape *shape)
+{
+    Shape s;
+    if (check(shape, &s) != ATTN_OK)
+        return 0;
+    return effective_splits(shape);
+}
+
+int attn_device_cu_count(int device, int32_t *cus)
+{
+    if (!cus)
+        return fail(ATTN_ERR_INVALID_ARG, "cus is NULL");
+    int n = 0;
+    const hipError_t e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipDeviceGetAttribute");
+    *cus = n;
+    return ok();
+}
+
+int attn_plan(const attn_shape *shape, const int32_t *lengths, const int32_t *page_table,
+              void *workspace, size_t workspace_bytes, void *stream)
+{
+    (void)page_table;
+    Shape s;
+    WsLayout L;
+    int rc = check(shape, &s);
+    if (rc != ATTN_OK)
+        return rc;
+    if (!lengths)
+        return fail(ATTN_ERR_INVALID_ARG, "lengths is NULL");
+    if ((rc = check_ws(s, workspace, workspace_bytes, &L)) != ATTN_OK)
+        return rc;
+    PlanArgs a;
+    a.lengths = lengths;
+    a.header = at<int32_t>(workspace, L.header);
+    a.len_eff = at<int32_t>(workspace, L.len_eff);
+    a.tiles_prefix = at<int32_t>(workspace, L.tiles_prefix);
+    a.seg_prefix = at<int32_t>(workspace, L.seg_prefix);
+    a.first_wg = at<int32_t>(workspace, L.first_wg);
+    a.wg_begin = at<int32_t>(workspace, L.wg_begin);
+    a.wg_start_b = at<int32_t>(workspace, L.wg_start_b);
+    a.B = s.B;
+    a.Hkv = s.Hkv;
+    a.P = s.P;
+    a.pt_stride = s.pt_stride;
+    a.T = s.T;
+    a.W = s.W;
+    a.mode = s.mode;
+    a.S = s.S;
+    const hipError_t e = launch_plan(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "plan launch");
+    return ok();
+}
+
+int attn_decode(const attn_shape *shape, const void *q, const void *k_cache, const void *v_cache,
+                const float *k_scale, const float *v_scale, const int32_t *page_table,
+                float sm_scale, void *workspace, size_t workspace_bytes, void *out, float *lse,
+                void *stream)
+{
+    Shape s;
+    WsLayout L;
+    int rc = check(shape, &s);
+    if (rc != ATTN_OK)
+        return rc;
+    if (!q || !k_cache || !v_cache || !page_table || !out)
+        return fail(ATTN_ERR_INVALID_ARG, "q, k_cache, v_cache, page_table and out must be non-NULL");
+    if (s.kv_fp8 && (!k_scale || !v_scale))
+        return fail(ATTN_ERR_INVALID_ARG, "fp8 cache needs k_scale and v_scale");
+    if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY)
+        return fail(ATTN_ERR_INVALID_ARG, "sm_scale is not finite");
+    if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
+         reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(out)) % 16)
+        return fail(ATTN_ERR_INVALID_ARG, "q, caches and out must be 16-byte aligned");
+    if ((rc = check_ws(s, workspace, workspace_bytes, &L)) != ATTN_OK)
+        return rc;
+    DecodeArgs a;
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint8_t *>(k_cache);
+    a.v = static_cast<const uint8_t *>(v_cache);
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.page_table = page_table;
+    a.header = at<int32_t>(workspace, L.header);
+    a.len_eff = at<int32_t>(workspace, L.len_eff);
+    a.tiles_prefix = at<int32_t>(workspace, L.tiles_prefix);
+    a.seg_prefix = at<int32_t>(workspace, L.seg_prefix);
+    a.first_wg = at<int32_t>(workspace, L.first_wg);
+    a.wg_begin = at<int32_t>(workspace, L.wg_begin);
+    a.wg_start_b = at<int32_t>(workspace, L.wg_start_b);
+    a.part_o = at<float>(workspace, L.part_o);
+    a.part_lse = at<float>(workspace, L.part_lse);
+    a.out = static_cast<uint16_t *>(out);
+    a.lse = lse;
+    a.B = s.B;
+    a.Hq = s.Hq;
+    a.Hkv = s.Hkv;
+    a.G = s.G;
+    a.P = s.P;
+    a.num_pages = s.num_pages;
+    a.pt_stride = s.pt_stride;
+    a.blocks_per_tile = s.T / kBlockTokens;
+    a.S = s.S;
+    a.scale_log2 = sm_scale * 1.4426950408889634f;
+    const int grid = s.mode == ATTN_STATIC ? s.B * s.Hkv * s.S : s.W;
+    const hipError_t e = launch_decode(a, s.mode, s.kv_fp8, grid, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "decode launch");
+    return ok();
+}
+
+int attn_combine(const attn_shape *shape, const void *workspace, size_t workspace_bytes, void *out,
+                 float *lse, void *stream)
+{
+    Shape s;
+    WsLayout L;
+    int rc = check(shape, &s);
+    if (rc != ATTN_OK)
+        return rc;
+    if (!out)
+        return fail(ATTN_ERR_INVALID_ARG, "out is NULL");
+    if (reinterpret_cast<uintptr_t>(out) % 16)
+        return fail(ATTN_ERR_INVALID_ARG, "out must be 16-byte aligned");
+    if ((rc = check_ws(s, workspace, workspace_bytes, &L)) != ATTN_OK)
+        return rc;
+    CombineArgs a;
+    a.header = at<int32_t>(workspace, L.header);
+    a.seg_prefix = at<int32_t>(workspace, L.seg_prefix);
+    a.part_o = at<float>(workspace, L.part_o);
+    a.part_lse = at<float>(workspace, L.part_lse);
+    a.out = static_cast<uint16_t *>(out);
+    a.lse = lse;
+    a.B = s.B;
+    a.Hq = s.Hq;
+    a.Hkv = s.Hkv;
+    a.G = s.G;
+    a.mode = s.mode;
+    a.S = s.S;
+    const hipError_t e = launch_combine(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "combine launch");
+    return ok();
+}
+
+int attn_get_status(const void *workspace, uint32_t *flags, void *stream)
+{
+    if (!workspace || !flags)
+        return fail(ATTN_ERR_INVALID_ARG, "workspace and flags must be non-NULL");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(flags, workspace, sizeof(uint32_t), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(st);
+    if (e != hipSuccess)
+        return hip_fail(e, "status copy");
+    return ok();
+}
+
+int attn_read_plan(const attn_shape *shape, const void *workspace, int32_t *header, int32_t *len_eff,
+                   int32_t *tiles_prefix, int32_t *seg_prefix, int32_t *first_wg, int32_t *wg_begin,
+                   int32_t *wg_start_b, void *stream)
+{
+    Shape s;
+    int rc = check(shape, &s);
+    if (rc != ATTN_OK)
+        return rc;
+    if (!workspace)
+        return fail(ATTN_ERR_INVALID_ARG, "workspace is NULL");
+    const WsLayout L = ws_layout(s);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t nbg = (int64_t)s.B * s.Hkv;
+    struct Item {
+        int32_t *dst;
+        size_t off;
+        int64_t n;
+    } items[] = {
+        {header, L.header, kHeaderInts},      {len_eff, L.len_eff, s.B},
+        {tiles_prefix, L.tiles_prefix, s.B + 1}, {seg_prefix, L.seg_prefix, nbg + 1},
+        {first_wg, L.first_wg, nbg},           {wg_begin, L.wg_begin, s.W + 1},
+        {wg_start_b, L.wg_start_b, s.W},
+    };
+    for (const Item &it : items) {
+        if (!it.dst)
+            continue;
+        const hipError_t e = hipMemcpyAsync(it.dst, at<int32_t>(workspace, it.off),
+                                            sizeof(int32_t) * it.n, hipMemcpyDeviceToHost, st);
+        if (e != hipSuccess)
+            return hip_fail(e, "plan copy");
+    }
+    const hipError_t e = hipStreamSynchronize(st);
+    if (e != hipSuccess)
+        return hip_fail(e, "plan copy sync");
+    return ok();
+}
+
+const char *attn_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// Internal declarations shared by the planner, decode/combine kernels and the
+// C ABI of libvlkv_attn.so. Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace vlkv {
+
+constexpr int kHeadDim = 128;      // D supported by the decode kernel
+constexpr int kWaves = 4;          // wavefronts per decode workgroup
+constexpr int kSlice = 16;         // tokens per wave per 64-token block
+constexpr int kBlockTokens = 64;   // kWaves * kSlice
+constexpr int kDecodeThreads = 256;
+constexpr int kMaxGroup = 16;      // query heads per kv head (one MFMA column block)
+constexpr int kPlanThreads = 1024;
+constexpr int kMaxBatch = 8192;    // planner keeps the tile prefix in LDS
+constexpr int kHeaderInts = 8;
+
+// header fields
+enum : int { H_STATUS = 0, H_UNITS = 1, H_WEFF = 2, H_MAXLEN = 3, H_CHUNK = 4, H_SPLITS = 5,
+             H_TILES = 6, H_TILE = 7 };
+
+// Byte offsets of the workspace regions (all 256-B aligned).
+struct WsLayout {
+    size_t header, len_eff, tiles_prefix, seg_prefix, first_wg, wg_begin, wg_start_b;
+    size_t part_lse, part_o, total;
+    int64_t max_slots;
+};
+
+struct Shape {
+    int B, Hq, Hkv, G, D, P, num_pages, pt_stride, T, W, kv_fp8, mode, S;
+};
+
+WsLayout ws_layout(const Shape &s);
+
+struct PlanArgs {
+    const int32_t *lengths;
+    int32_t *header, *len_eff, *tiles_prefix, *seg_prefix, *first_wg, *wg_begin, *wg_start_b;
+    int B, Hkv, P, pt_stride, T, W, mode, S;
+};
+
+struct DecodeArgs {
+    const uint16_t *q;         // [B][Hq][D] bf16 bits
+    const uint8_t *k;          // cache base (bytes)
+    const uint8_t *v;
+    const float *k_scale, *v_scale;
+    const int32_t *page_table;
+    int32_t *header;
+    const int32_t *len_eff, *tiles_prefix, *seg_prefix, *first_wg, *wg_begin, *wg_start_b;
+    float *part_o, *part_lse;
+    uint16_t *out;             // [B][Hq][D] bf16 bits
+    float *lse;                // [B][Hq] or null
+    int B, Hq, Hkv, G, P, num_pages, pt_stride, blocks_per_tile, S;
+    float scale_log2;          // sm_scale * log2(e)
+};
+
+struct CombineArgs {
+    const int32_t *header, *seg_prefix;
+    const float *part_o, *part_lse;
+    uint16_t *out;
+    float *lse;
+    int B, Hq, Hkv, G, mode, S;
+};
+
+hipError_t launch_plan(const PlanArgs &a, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs &a, int mode, int kv_fp8, int grid, hipStream_t st);
+hipError_t launch_combine(const CombineArgs &a, hipStream_t st);
+
+}  // namespace vlkv

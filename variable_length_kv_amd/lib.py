@@ -1,0 +1,219 @@
+"""ctypes binding of libvlkv_attn.so (the C ABI in include/vlkv_attn.h).
+
+Argument marshalling only: every step of the attention path runs in the HIP
+library. Tensors are PyTorch device tensors (torch provides device memory and
+the current stream); the functions take the same names as the C entry points.
+If the library has not been built this module raises on first use: there is
+no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvlkv_attn.so")
+
+ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
+ATTN_KV_BF16, ATTN_KV_FP8_E4M3 = 0, 1
+ATTN_DYNAMIC, ATTN_STATIC = 0, 1
+ATTN_STATUS_BAD_LENGTH, ATTN_STATUS_BAD_PAGE = 1, 2
+
+EXPORTED = ("attn_check_shape", "attn_workspace_bytes", "attn_static_splits", "attn_device_cu_count",
+            "attn_plan", "attn_decode", "attn_combine", "attn_get_status", "attn_read_plan",
+            "attn_last_error")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "num_q_heads", "num_kv_heads", "head_dim", "page_size", "num_pages", "pt_stride",
+        "tile_tokens", "num_wgs", "kv_dtype", "mode", "static_splits")]
+
+
+@dataclass
+class AttnShape:
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    page_size: int
+    num_pages: int
+    pt_stride: int
+    num_wgs: int
+    head_dim: int = 128
+    tile_tokens: int = 64
+    kv_dtype: int = ATTN_KV_BF16
+    mode: int = ATTN_DYNAMIC
+    static_splits: int = 0
+
+    def c(self) -> _Shape:
+        return _Shape(self.batch, self.num_q_heads, self.num_kv_heads, self.head_dim, self.page_size,
+                      self.num_pages, self.pt_stride, self.tile_tokens, self.num_wgs, self.kv_dtype,
+                      self.mode, self.static_splits)
+
+
+_lib = None
+
+
+def load():
+    """Load libvlkv_attn.so (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m variable_length_kv_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    SP = ctypes.POINTER(_Shape)
+    sigs = {
+        "attn_check_shape": (i32, [SP]),
+        "attn_workspace_bytes": (sz, [SP]),
+        "attn_static_splits": (i32, [SP]),
+        "attn_device_cu_count": (i32, [ctypes.c_int, P]),
+        "attn_plan": (i32, [SP, P, P, P, sz, P]),
+        "attn_decode": (i32, [SP, P, P, P, P, P, P, ctypes.c_float, P, sz, P, P, P]),
+        "attn_combine": (i32, [SP, P, sz, P, P, P]),
+        "attn_get_status": (i32, [P, P, P]),
+        "attn_read_plan": (i32, [SP, P, P, P, P, P, P, P, P, P]),
+        "attn_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(rc):
+    if rc != ATTN_OK:
+        raise AttnError(rc, load().attn_last_error().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, torch.Tensor):
+        if not t.is_contiguous():
+            raise ValueError("tensors passed to the attention library must be contiguous")
+        return ctypes.c_void_p(t.data_ptr())
+    return ctypes.c_void_p(int(t))
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _shape(shape):
+    s = shape.c() if isinstance(shape, AttnShape) else shape
+    return ctypes.byref(s)
+
+
+def attn_check_shape(shape) -> None:
+    _check(load().attn_check_shape(_shape(shape)))
+
+
+def attn_workspace_bytes(shape) -> int:
+    n = load().attn_workspace_bytes(_shape(shape))
+    if n == 0:
+        attn_check_shape(shape)
+    return int(n)
+
+
+def attn_static_splits(shape) -> int:
+    return int(load().attn_static_splits(_shape(shape)))
+
+
+def attn_device_cu_count(device: int = 0) -> int:
+    out = ctypes.c_int32()
+    _check(load().attn_device_cu_count(int(device), ctypes.byref(out)))
+    return int(out.value)
+
+
+def attn_plan(shape, lengths, page_table, workspace, stream=None) -> None:
+    _check(load().attn_plan(_shape(shape), _ptr(lengths), _ptr(page_table), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def attn_decode(shape, q, k_cache, v_cache, k_scale, v_scale, page_table, sm_scale, workspace, out,
+                lse=None, stream=None) -> None:
+    _check(load().attn_decode(_shape(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                              _ptr(v_scale), _ptr(page_table), float(sm_scale), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
+                              _stream(stream)))
+
+
+def attn_combine(shape, workspace, out, lse=None, stream=None) -> None:
+    _check(load().attn_combine(_shape(shape), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def attn_get_status(workspace, stream=None) -> int:
+    out = ctypes.c_uint32()
+    _check(load().attn_get_status(_ptr(workspace), ctypes.byref(out), _stream(stream)))
+    return int(out.value)
+
+
+def attn_read_plan(shape, workspace, stream=None) -> dict:
+    import numpy as np
+    B, Hkv, W = shape.batch, shape.num_kv_heads, shape.num_wgs
+    out = {
+        "header": np.zeros(8, np.int32), "len_eff": np.zeros(B, np.int32),
+        "tiles_prefix": np.zeros(B + 1, np.int32), "seg_prefix": np.zeros(B * Hkv + 1, np.int32),
+        "first_wg": np.zeros(B * Hkv, np.int32), "wg_begin": np.zeros(W + 1, np.int32),
+        "wg_start_b": np.zeros(W, np.int32),
+    }
+    keys = ("header", "len_eff", "tiles_prefix", "seg_prefix", "first_wg", "wg_begin", "wg_start_b")
+    _check(load().attn_read_plan(_shape(shape), _ptr(workspace),
+                                 *[ctypes.c_void_p(out[k].ctypes.data) for k in keys], _stream(stream)))
+    return out
+
+
+class Attention:
+    """One decode-attention configuration with its own workspace.
+
+    ``step`` enqueues attn_plan, attn_decode and attn_combine on the current
+    stream. The workspace is a torch uint8 tensor (device memory only).
+    """
+
+    def __init__(self, shape: AttnShape, device="cuda"):
+        self.shape = shape
+        n = attn_workspace_bytes(shape)
+        self.workspace = torch.empty(n + 256, dtype=torch.uint8, device=device)
+        off = (-self.workspace.data_ptr()) % 256
+        self.workspace = self.workspace[off:off + n]
+
+    def plan(self, lengths, page_table, stream=None):
+        attn_plan(self.shape, lengths, page_table, self.workspace, stream)
+
+    def decode(self, q, k_cache, v_cache, page_table, sm_scale, out, lse=None, k_scale=None,
+               v_scale=None, stream=None):
+        attn_decode(self.shape, q, k_cache, v_cache, k_scale, v_scale, page_table, sm_scale,
+                    self.workspace, out, lse, stream)
+
+    def combine(self, out, lse=None, stream=None):
+        attn_combine(self.shape, self.workspace, out, lse, stream)
+
+    def step(self, q, k_cache, v_cache, page_table, lengths, sm_scale, out, lse=None, k_scale=None,
+             v_scale=None, stream=None):
+        self.plan(lengths, page_table, stream)
+        self.decode(q, k_cache, v_cache, page_table, sm_scale, out, lse, k_scale, v_scale, stream)
+        self.combine(out, lse, stream)
+
+    def status(self, stream=None) -> int:
+        return attn_get_status(self.workspace, stream)
+
+    def read_plan(self, stream=None) -> dict:
+        return attn_read_plan(self.shape, self.workspace, stream)
