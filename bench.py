@@ -1,0 +1,282 @@
+"""Benchmark: one decode-attention step (plan + split-KV decode + combine) on
+one MI355X, through the C ABI of libvlkv_attn.so.
+
+Default workload (the headline): 32 requests with context lengths uniform in
+[1000, 16000], 64 query / 8 kv heads, head dim 128, bf16 paged cache with
+64-token pages. A step is attn_plan + attn_decode + attn_combine over the whole
+batch; K steps run back to back between two device synchronisations. The
+figure of merit is effective KV bandwidth: every cached K and V row of the
+batch once (2 * Hkv * D * 2 bytes per token) divided by the step time.
+
+Also reported (field "extra"): the skewed batch (1 x 16000 + 63 x 1000
+tokens) under the dynamic plan and under the in-library static split-K at its
+default split count and a split sweep, and the long-tail batch. Those are
+timed per step with HIP events, with a 1 GiB read sweep between steps so that no
+step starts with the previous step's data in the 256 MB Infinity Cache.
+
+Prints ONE JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attention µs/step and effective KV GB/s (% of HBM peak), mixed lengths"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic_uniform_mixed.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in ("decode.hip", "vlkv_internal.hpp"):
+        with open(os.path.join(ROOT, "variable_length_kv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+class Runner:
+    """Device copies of one decode step and an Attention object per mode."""
+
+    def __init__(self, case, torch, L, W):
+        self.c, self.torch, self.L = case, torch, L
+        d = torch.device("cuda:0")
+        self.q = case.q.to(d)
+        self.k = case.k_cache.to(d)
+        self.v = case.v_cache.to(d)
+        self.ks = case.k_scale.to(d) if case.k_scale is not None else None
+        self.vs = case.v_scale.to(d) if case.v_scale is not None else None
+        self.pt = torch.from_numpy(np.ascontiguousarray(case.page_table)).to(d)
+        self.len = torch.from_numpy(np.ascontiguousarray(case.lengths, np.int32)).to(d)
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty(case.B, case.Hq, dtype=torch.float32, device=d)
+        self.W = W
+
+    def attention(self, mode, S=0):
+        c, L = self.c, self.L
+        shape = L.AttnShape(batch=c.B, num_q_heads=c.Hq, num_kv_heads=c.Hkv, page_size=c.P,
+                            num_pages=c.num_pages, pt_stride=c.pt_stride, num_wgs=self.W,
+                            kv_dtype=L.ATTN_KV_FP8_E4M3 if c.kv_dtype == "fp8" else L.ATTN_KV_BF16,
+                            mode=mode, static_splits=S)
+        return L.Attention(shape, "cuda:0")
+
+    def plan(self, att):
+        att.plan(self.len, self.pt)
+
+    def decode(self, att):
+        att.decode(self.q, self.k, self.v, self.pt, self.c.sm_scale, self.out, self.lse, self.ks, self.vs)
+
+    def combine(self, att):
+        att.combine(self.out, self.lse)
+
+    def step(self, att):
+        self.plan(att)
+        self.decode(att)
+        self.combine(att)
+
+
+def timed_steps(run, att, steps, warmup, torch):
+    """K back-to-back steps between two synchronisations, with HIP events
+    around each launch on the stream the library launches on."""
+    for _ in range(warmup):
+        run.step(att)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(steps):
+        ev[i][0].record()
+        run.plan(att)
+        ev[i][1].record()
+        run.decode(att)
+        ev[i][2].record()
+        run.combine(att)
+        ev[i][3].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    per = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in ev])  # ms
+    return total_ms / steps, per, wall
+
+
+def per_step_flushed(run, att, steps, warmup, torch, flush):
+    """Steps timed one at a time (events around plan..combine), with a cache
+    flush between them. Returns per-step ms."""
+    for _ in range(warmup):
+        run.step(att)
+    ts = []
+    for _ in range(steps):
+        flush.sum()  # read-only sweep: evicts the step's data, leaves no dirty lines
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        run.step(att)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    return np.array(ts)
+
+
+def cpu_baseline(case, budget_s=20.0):
+    """The CPU reference (fp64 C, OpenMP) on a bounded sample of the same
+    workload: whole requests, taken in index order until the budget is spent."""
+    import oracle
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    done, tokens, t_total = [], 0, 0.0
+    for b in range(case.B):
+        t0 = time.perf_counter()
+        oracle.decode(case, [b], threads=threads)
+        dt = time.perf_counter() - t0
+        done.append(b)
+        tokens += int(case.lengths[b])
+        t_total += dt
+        if t_total >= budget_s:
+            break
+    nbytes = 2 * case.Hkv * case.D * case.elem_bytes * tokens
+    return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(done)} of {case.B} requests ({tokens} tokens, {nbytes / 1e6:.1f} MB of KV), "
+                      f"{t_total:.1f} s, fp64 C with OpenMP over (request, kv head)"}
+
+
+def traffic_entry(decode_ms_avg):
+    """HBM bytes per decode launch from committed rocprofv3 counters, only if
+    they were taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("source_hash") != source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--wgs-per-cu", type=int, default=2)
+    ap.add_argument("--no-extra", action="store_true", help="headline workload only")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would run its own "
+              "requests' plan independently); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from variable_length_kv_amd import lib as L
+    from variable_length_kv_amd import workloads as wl
+    L.load()
+    cus = L.attn_device_cu_count(0)
+    W = args.wgs_per_cu * cus
+
+    # ---- headline: uniform-mixed batch, dynamic plan ------------------------
+    t0 = time.perf_counter()
+    c1 = wl.config_case(1)
+    log(f"bench: workload 1 generated in {time.perf_counter() - t0:.1f} s "
+        f"({c1.kv_bytes / 1e9:.3f} GB of KV, {c1.total_tokens} tokens)")
+    r1 = Runner(c1, torch, L, W)
+    att = r1.attention(L.ATTN_DYNAMIC)
+    ms, per, wall = timed_steps(r1, att, args.steps, args.warmup, torch)
+    plan_ms, dec_ms, comb_ms = per.mean(axis=0)
+    log(f"bench: headline {ms * 1e3:.1f} us/step (plan {plan_ms * 1e3:.1f}, decode {dec_ms * 1e3:.1f}, "
+        f"combine {comb_ms * 1e3:.1f}); wall {wall:.2f} s")
+    kv = c1.kv_bytes
+    value = kv / (ms * 1e-3) / 1e9
+    achieved = kv / (dec_ms * 1e-3) / 1e9
+    traffic = traffic_entry(dec_ms)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "uniform-mixed: 32 requests, lengths U[1000,16000] (seed 0, 284965 tokens), "
+                               "64 q / 8 kv heads, head_dim 128, bf16 KV, page 64, random page table",
+                   "global_batch": c1.B, "seq_len": int(c1.lengths.max()), "parallelism": "single GPU",
+                   "tile_tokens": 64, "num_wgs": W, "us_per_step": round(ms * 1e3, 2),
+                   "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+                   "breakdown_us": {"plan": round(plan_ms * 1e3, 2), "decode": round(dec_ms * 1e3, 2),
+                                    "combine": round(comb_ms * 1e3, 2)}},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "decode_kernel<dynamic, bf16>",
+                     "algorithmic_bytes_per_launch": kv,
+                     "decode_avg_us": round(dec_ms * 1e3, 2)},
+    }
+    del att, r1
+    torch.cuda.empty_cache()
+
+    # ---- extra workloads ------------------------------------------------------
+    if not args.no_extra:
+        extra = {}
+        flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+        for cid, label in ((2, "skewed"), (3, "long_tail")):
+            c = wl.config_case(cid)
+            r = Runner(c, torch, L, W)
+            entry = {"kv_gb": round(c.kv_bytes / 1e9, 4), "tokens": c.total_tokens}
+            a = r.attention(L.ATTN_DYNAMIC)
+            t = per_step_flushed(r, a, 30, 5, torch, flush)
+            entry["dynamic_us_median"] = round(float(np.median(t)) * 1e3, 2)
+            entry["dynamic_us_p90"] = round(float(np.percentile(t, 90)) * 1e3, 2)
+            entry["dynamic_pct_hbm"] = round(100 * c.kv_bytes / (np.median(t) * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)
+            ms_b2b, per_b2b, _ = timed_steps(r, a, 30, 5, torch)
+            entry["dynamic_us_back_to_back"] = round(ms_b2b * 1e3, 2)
+            entry["dynamic_decode_us_back_to_back"] = round(float(per_b2b[:, 1].mean()) * 1e3, 2)
+            del a
+            if cid == 2:
+                st = {}
+                S_def = None
+                for S in (0, 1, 2, 4, 8, 16, 32, 64):
+                    a = r.attention(L.ATTN_STATIC, S)
+                    S_eff = L.attn_static_splits(a.shape)
+                    t = per_step_flushed(r, a, 20, 3, torch, flush)
+                    if S == 0:
+                        S_def = S_eff
+                        entry["static_default_splits"] = S_eff
+                        entry["static_default_us_median"] = round(float(np.median(t)) * 1e3, 2)
+                    else:
+                        st[str(S)] = round(float(np.median(t)) * 1e3, 2)
+                    del a
+                entry["static_sweep_us_median"] = st
+                best = min(st.values())
+                entry["speedup_vs_static_default"] = round(entry["static_default_us_median"] /
+                                                           entry["dynamic_us_median"], 3)
+                entry["speedup_vs_best_static"] = round(best / entry["dynamic_us_median"], 3)
+            extra[label] = entry
+            log(f"bench: {label}: {json.dumps(entry)}")
+            del r
+            torch.cuda.empty_cache()
+        del flush
+        result["extra"] = extra
+
+    # ---- CPU baseline (the oracle, bounded sample of the headline workload) ---
+    result["cpu_baseline"] = cpu_baseline(c1, args.cpu_budget)
+    log(f"bench: cpu baseline {result['cpu_baseline']}")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

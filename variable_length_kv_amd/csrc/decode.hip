@@ -49,6 +49,16 @@ constexpr int kLdsRow = kHeadDim + 4;  // padded fp32 row of the merge buffer
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Read-only data of the step (plan arrays, page table, scales) is read through
+// the constant address space: wave-uniform addresses then become scalar loads,
+// which are counted apart from the K/V vector loads, so waiting for a page id
+// never waits for K/V data still in flight.
+template <typename T>
+__device__ __forceinline__ T ldc(const T *p, size_t i)
+{
+    return ((const __attribute__((address_space(4))) T *)(p))[i];
+}
+
 // max / sum over lanes l, l^16, l^32, l^48 (the 4 row groups of an MFMA tile)
 __device__ __forceinline__ float xmax4(float x)
 {
@@ -116,9 +126,9 @@ struct Walker {
         const int nblk = (L + kBlockTokens - 1) / kBlockTokens;
         blk_end = min(tb * R, nblk);
         const int bg = b * a->Hkv + g;
-        const int s0 = a->seg_prefix[bg];
-        const int s1 = a->seg_prefix[bg + 1];
-        slot = s0 + (w - a->first_wg[bg]);
+        const int s0 = ldc(a->seg_prefix, bg);
+        const int s1 = ldc(a->seg_prefix, bg + 1);
+        slot = s0 + (w - ldc(a->first_wg, bg));
         direct = (s1 - s0) == 1;
     }
 
@@ -129,12 +139,12 @@ struct Walker {
         wave = wv;
         done = 0;
         if (MODE == 0) {
-            const int u0 = a->wg_begin[w];
-            const int u1 = a->wg_begin[w + 1];
-            b = a->wg_start_b[w];
-            const int tp0 = a->tiles_prefix[b];
-            nt = a->tiles_prefix[b + 1] - tp0;
-            L = a->len_eff[b];
+            const int u0 = ldc(a->wg_begin, w);
+            const int u1 = ldc(a->wg_begin, w + 1);
+            b = ldc(a->wg_start_b, w);
+            const int tp0 = ldc(a->tiles_prefix, b);
+            nt = ldc(a->tiles_prefix, b + 1) - tp0;
+            L = ldc(a->len_eff, b);
             const int rem = u0 - tp0 * a->Hkv;
             g = rem / nt;
             const int t = rem - g * nt;
@@ -146,8 +156,8 @@ struct Walker {
             const int bg = w / S, s = w - bg * S;
             b = bg / a->Hkv;
             g = bg - b * a->Hkv;
-            L = a->len_eff[b];
-            const int C = a->header[H_CHUNK];
+            L = ldc(a->len_eff, b);
+            const int C = ldc(a->header, H_CHUNK);
             const int lo = s * C, hi = min(lo + C, L);
             units_left = 0;
             slot = w;
@@ -164,7 +174,33 @@ struct Walker {
         }
     }
 
-    // Describe the current block and step to the next one.
+    // Number of blocks this workgroup will process (a scalar walk over its
+    // segments; the walker itself is not advanced).
+    __device__ int count_blocks() const
+    {
+        if (MODE != 0)
+            return blk_end - blk;
+        int n = blk_end - blk;
+        int bb = b, gg = g, ntt = nt, LL = L, left = units_left;
+        const int R = a->blocks_per_tile;
+        while (left > 0) {
+            if (++gg == a->Hkv) {
+                gg = 0;
+                do {
+                    ++bb;
+                    ntt = ldc(a->tiles_prefix, bb + 1) - ldc(a->tiles_prefix, bb);
+                } while (ntt == 0);
+                LL = ldc(a->len_eff, bb);
+            }
+            const int take = min(ntt, left);
+            left -= take;
+            n += min(take * R, (LL + kBlockTokens - 1) / kBlockTokens);
+        }
+        return n;
+    }
+
+    // Describe the current block and step to the next one. Past the end the
+    // description is invalid: no valid tokens, no segment start or end.
     __device__ Meta next()
     {
         Meta m;
@@ -172,9 +208,9 @@ struct Walker {
         m.b = b;
         m.g = g;
         m.tok0 = blk * kBlockTokens + wave * kSlice;
-        m.nv = max(0, min(kSlice, L - m.tok0));
-        m.first = blk == blk0;
-        m.last = blk + 1 == blk_end;
+        m.nv = done ? 0 : max(0, min(kSlice, L - m.tok0));
+        m.first = !done && blk == blk0;
+        m.last = !done && blk + 1 == blk_end;
         m.slot = slot;
         m.direct = direct;
         m.ksc = 1.f;
@@ -189,9 +225,9 @@ struct Walker {
                     g = 0;
                     do {
                         ++b;
-                        nt = a->tiles_prefix[b + 1] - a->tiles_prefix[b];
+                        nt = ldc(a->tiles_prefix, b + 1) - ldc(a->tiles_prefix, b);
                     } while (nt == 0);
-                    L = a->len_eff[b];
+                    L = ldc(a->len_eff, b);
                 }
                 const int take = min(nt, units_left);
                 units_left -= take;
@@ -208,7 +244,7 @@ template <int MODE, int KVFP8>
 __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
 {
     const int w = blockIdx.x;
-    if (MODE == 0 && w >= a.header[H_WEFF])
+    if (MODE == 0 && w >= ldc(a.header, H_WEFF))
         return;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -218,6 +254,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
     __shared__ __attribute__((aligned(16))) float lds_acc[kWaves][kMaxGroup][kLdsRow];
     __shared__ float lds_m[kWaves][kMaxGroup];
     __shared__ float lds_l[kWaves][kMaxGroup];
+    __shared__ float lds_e[kWaves][kMaxGroup];
 
     const int G = a.G;
     constexpr int D = kHeadDim;
@@ -245,7 +282,9 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
 
     // per-wave softmax state, head = row. m_run is uniform over the 4 row
     // groups; l_run is this lane's partial sum, reduced at segment end.
-    float m_run = -INFINITY, l_run = 0.f, sc = a.scale_log2, vsc_run = 1.f;
+    // l_run sums the bf16-rounded weights that multiply V (normalises o exactly
+    // like P.V); e_run sums the unrounded fp32 weights (gives an accurate lse).
+    float m_run = -INFINITY, l_run = 0.f, e_run = 0.f, sc = a.scale_log2, vsc_run = 1.f;
     f32x4 acc[8];
     u32x4 qreg[4];
 #pragma unroll
@@ -255,66 +294,72 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
     for (int i = 0; i < 4; ++i)
         qreg[i] = u32x4{0u, 0u, 0u, 0u};
 
+    int bad_page = 0;
+
     // ---- loads of one block into a slot ---------------------------------
+    // K/V loads are issued for every slot, also past the end of the work or
+    // for an empty or invalid slice (then from page 0, which always exists, and
+    // never used), so the number of vector loads between any two points of the
+    // pipeline is fixed and the wait before each compute covers its own slot only.
     auto issue = [&](Slot &s, Meta &mt) {
         mt = wk.next();
-        if (!mt.valid)
-            return;
-        if (mt.first) {
-            // q of (b, g) as the B operand: head = row (zero beyond G), dims as K
-            if (row < G) {
-                const uint16_t *qp = a.q + ((size_t)mt.b * a.Hq + (size_t)mt.g * G + row) * D;
+        if (mt.valid && mt.first) {
+            // q of (b, g) as the B operand: head = row. Branch-free: rows >= G
+            // read head 0 and are zeroed when copied at the segment's first block,
+            // so nothing here waits for the load and no divergent control flow
+            // separates the scalar bookkeeping of the pipeline.
+            const int hrow = row < G ? row : 0;
+            const uint16_t *qp = a.q + ((size_t)mt.b * a.Hq + (size_t)mt.g * G + hrow) * D;
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const int d0 = KVFP8 ? 16 * grp + 64 * (kk >> 1) + 8 * (kk & 1) : 32 * kk + 8 * grp;
-                    s.q[kk] = *reinterpret_cast<const u32x4 *>(qp + d0);
-                }
-            } else {
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    s.q[kk] = u32x4{0u, 0u, 0u, 0u};
+            for (int kk = 0; kk < 4; ++kk) {
+                const int d0 = KVFP8 ? 16 * grp + 64 * (kk >> 1) + 8 * (kk & 1) : 32 * kk + 8 * grp;
+                s.q[kk] = *reinterpret_cast<const u32x4 *>(qp + d0);  // zeroed at use
             }
             if (KVFP8) {
-                mt.ksc = a.k_scale[mt.b * a.Hkv + mt.g];
-                mt.vsc = a.v_scale[mt.b * a.Hkv + mt.g];
+                mt.ksc = ldc(a.k_scale, (size_t)mt.b * a.Hkv + mt.g);
+                mt.vsc = ldc(a.v_scale, (size_t)mt.b * a.Hkv + mt.g);
             }
         }
-        if (mt.nv > 0) {
-            const int page = a.page_table[(size_t)mt.b * a.pt_stride + mt.tok0 / a.P];
+        size_t off = (size_t)mt.g * page_head_bytes + (size_t)row * (D * EB);  // page 0
+        if (mt.valid && mt.nv > 0) {
+            const int page = ldc(a.page_table, (size_t)mt.b * a.pt_stride + mt.tok0 / a.P);
             if (page < 0 || page >= a.num_pages) {
-                if (lane == 0)
-                    atomicOr(reinterpret_cast<unsigned *>(a.header + H_STATUS), 2u);
+                bad_page = 1;   // reported once at the end of the kernel
                 mt.nv = 0;
-                return;
-            }
-            const size_t off = ((size_t)page * a.Hkv + mt.g) * page_head_bytes +
-                               (size_t)(mt.tok0 % a.P + row) * (D * EB);
-            const uint8_t *kp = a.k + off;
-            const uint8_t *vp = a.v + off;
-            if (KVFP8) {
-#pragma unroll
-                for (int p = 0; p < 2; ++p) {
-                    s.k[p] = *reinterpret_cast<const u32x4 *>(kp + 16 * grp + 64 * p);
-                    s.v[p] = *reinterpret_cast<const u32x4 *>(vp + 16 * grp + 64 * p);
-                }
             } else {
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    s.k[kk] = *reinterpret_cast<const u32x4 *>(kp + 64 * kk + 16 * grp);
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    s.v[kk] = *reinterpret_cast<const u32x4 *>(vp + 64 * kk + 16 * grp);
+                off = ((size_t)page * a.Hkv + mt.g) * page_head_bytes +
+                      (size_t)(mt.tok0 % a.P + row) * (D * EB);
             }
+        }
+        if (!mt.valid)
+            off = (size_t)row * (D * EB);
+        const uint8_t *kp = a.k + off;
+        const uint8_t *vp = a.v + off;
+        if (KVFP8) {
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                s.k[p] = *reinterpret_cast<const u32x4 *>(kp + 16 * grp + 64 * p);
+                s.v[p] = *reinterpret_cast<const u32x4 *>(vp + 16 * grp + 64 * p);
+            }
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                s.k[kk] = *reinterpret_cast<const u32x4 *>(kp + 64 * kk + 16 * grp);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                s.v[kk] = *reinterpret_cast<const u32x4 *>(vp + 64 * kk + 16 * grp);
         }
     };
 
     // ---- end of a segment: merge the 4 waves and write ------------------
     auto finish = [&](const Meta &mt) {
         const float l_tot = xsum4(l_run);
+        const float e_tot = xsum4(e_run);
         if (row < G) {
             if (grp == 0) {
                 lds_m[wave][row] = m_run;
                 lds_l[wave][row] = l_tot;
+                lds_e[wave][row] = e_tot;
             }
 #pragma unroll
             for (int mb = 0; mb < 8; ++mb) {
@@ -338,17 +383,18 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
             f32x4 o = {0.f, 0.f, 0.f, 0.f};
             float lse2 = -INFINITY;
             if (M != -INFINITY) {
-                float den = 0.f;
+                float den = 0.f, ex = 0.f;
 #pragma unroll
                 for (int v = 0; v < kWaves; ++v) {
                     const float e = fast_exp2(lds_m[v][h] - M);
                     den += e * lds_l[v][h];
+                    ex += e * lds_e[v][h];
                     const f32x4 x = *reinterpret_cast<const f32x4 *>(&lds_acc[v][h][d4]);
                     o += e * x;
                 }
                 const float r = vsc_run / den;
                 o *= r;
-                lse2 = M + log2f(den);
+                lse2 = M + log2f(ex);
             }
             const size_t hq = (size_t)mt.b * a.Hq + (size_t)mt.g * G + h;
             if (mt.direct) {
@@ -367,19 +413,24 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
 
     // ---- math of one block ----------------------------------------------
     auto compute = [&](Slot &s, const Meta &mt) {
-        if (mt.first) {
+        // Every register of the slot is consumed on every path (q through a
+        // select, K/V by the math, which runs even for an empty slice and then
+        // contributes nothing), so the compiler's load-wait bookkeeping never
+        // sees a load whose registers are reloaded without being waited for.
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                qreg[kk] = s.q[kk];
+        for (int kk = 0; kk < 4; ++kk)
+            qreg[kk] = mt.first ? (row < G ? s.q[kk] : u32x4{0u, 0u, 0u, 0u}) : qreg[kk];
+        if (mt.first) {
             m_run = -INFINITY;
             l_run = 0.f;
+            e_run = 0.f;
 #pragma unroll
             for (int i = 0; i < 8; ++i)
                 acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
             sc = a.scale_log2 * mt.ksc;
             vsc_run = mt.vsc;
         }
-        if (mt.nv > 0) {
+        {
             // scores: S^T[token 4*grp+i][head row]
             f32x4 st = {0.f, 0.f, 0.f, 0.f};
             if (KVFP8) {
@@ -420,6 +471,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
             const bf16x4 pb = __builtin_convertvector(p, bf16x4);
             const f32x4 pr = __builtin_convertvector(pb, f32x4);
             l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+            e_run = e_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
             m_run = m_new;
 #pragma unroll
             for (int i = 0; i < 8; ++i)
@@ -454,20 +506,21 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
     };
 
     // ---- software pipeline: two slices in flight per wave ---------------
+    // A counted loop (the block count is known from the plan) with both slots
+    // handled in every iteration; a trailing invalid block does nothing.
+    const int nblk = wk.count_blocks();
     Slot s0, s1;
     Meta m0, m1;
     issue(s0, m0);
     issue(s1, m1);
-    while (true) {
-        if (!m0.valid)
-            break;
+    for (int it = 0; it < nblk; it += 2) {
         compute(s0, m0);
         issue(s0, m0);
-        if (!m1.valid)
-            break;
         compute(s1, m1);
         issue(s1, m1);
     }
+    if (bad_page && lane == 0)
+        atomicOr(reinterpret_cast<unsigned *>(a.header + H_STATUS), 2u);
 }
 
 // One workgroup per (request, kv head): merge its partial slots, or write the

@@ -1,4 +1,4 @@
-// Per-step tile planner (one workgroup of 1024 threads).
+// Per-step tile planner (one workgroup).
 //
 // The source article's Dynamic Attention cuts each request's KV-cache work into
 // uniform tiles, hands them to CTAs according to the current load, and rebuilds
@@ -17,102 +17,135 @@
 //   static  chunk C = ceil(max Le / S) rounded up to lcm(P, T); split s of a
 //           pair covers tokens [s*C, min((s+1)*C, Le_b)); slot = bg*S + s
 //
-// Work is O(B*Hkv + W) with one block-wide scan per array.
+// The work is O(B*Hkv + W) and latency-bound: each thread owns a contiguous
+// chunk of every array, so a prefix sum is one serial pass per thread, one
+// wave scan and one exchange of 4 wave totals through LDS.
 #include "vlkv_internal.hpp"
 
 namespace vlkv {
 namespace {
 
-// Inclusive scan of one int per thread across the workgroup; returns this
-// thread's inclusive prefix and the workgroup total in *total.
-__device__ int64_t block_inclusive_scan(int64_t v, int64_t *lds_waves, int64_t *total)
+constexpr int kPT = 256;  // planner threads
+constexpr int kPW = kPT / 64;
+
+__device__ __forceinline__ int wave_incl_scan(int x)
 {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int nwaves = blockDim.x >> 6;
-    int64_t x = v;
+    const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-        int64_t y = __shfl_up(x, off, 64);
+        const int y = __shfl_up(x, off, 64);
         if (lane >= off)
             x += y;
     }
-    if (lane == 63)
-        lds_waves[wave] = x;
-    __syncthreads();
-    if (wave == 0) {
-        int64_t w = lane < nwaves ? lds_waves[lane] : 0;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            int64_t y = __shfl_up(w, off, 64);
-            if (lane >= off)
-                w += y;
-        }
-        if (lane < nwaves)
-            lds_waves[lane] = w;  // inclusive totals of waves
-    }
-    __syncthreads();
-    const int64_t before = wave ? lds_waves[wave - 1] : 0;
-    *total = lds_waves[nwaves - 1];
-    __syncthreads();  // lds_waves is reused by the next call
-    return x + before;
+    return x;
 }
 
-__device__ int64_t gcd64(int64_t a, int64_t b)
+__device__ __forceinline__ int wave_max(int x)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        x = max(x, __shfl_xor(x, off, 64));
+    return x;
+}
+
+__device__ __forceinline__ int wave_or(int x)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        x |= __shfl_xor(x, off, 64);
+    return x;
+}
+
+// Exclusive prefix of one int per thread over the workgroup (in thread order);
+// *total receives the sum over all threads.
+__device__ int block_excl_scan(int v, int *lds, int *total)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int incl = wave_incl_scan(v);
+    if (lane == 63)
+        lds[wave] = incl;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int i = 0; i < kPW; ++i) {
+        const int t = lds[i];
+        before += i < wave ? t : 0;
+        all += t;
+    }
+    __syncthreads();  // lds is reused by the next scan
+    *total = all;
+    return before + incl - v;
+}
+
+// floor(x / d) for 0 <= x < 2^53, d > 0: double estimate, exact correction.
+__device__ __forceinline__ int64_t div_floor(int64_t x, int64_t d)
+{
+    int64_t q = (int64_t)((double)x / (double)d);
+    if (q * d > x)
+        --q;
+    else if ((q + 1) * d <= x)
+        ++q;
+    return q;
+}
+
+__device__ __forceinline__ int64_t gcd64(int64_t a, int64_t b)
 {
     while (b) {
-        int64_t t = a % b;
+        const int64_t t = a % b;
         a = b;
         b = t;
     }
     return a;
 }
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a)
+__global__ __launch_bounds__(kPT) void plan_kernel(PlanArgs a)
 {
     __shared__ int32_t tp[kMaxBatch + 1];   // tiles prefix
-    __shared__ int64_t scan_tmp[kPlanThreads / 64];
-    __shared__ int32_t red_max, red_status;
-    const int tid = threadIdx.x;
-    if (tid == 0) {
-        red_max = 0;
-        red_status = 0;
-        tp[0] = 0;
-    }
-    __syncthreads();
+    __shared__ int scan_lds[kPW];
+    __shared__ int red_lds[2 * kPW];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
 
-    // 1) validated lengths and tile prefix
+    // 1) validated lengths and the tiles prefix
     const int64_t limit = (int64_t)a.pt_stride * a.P;
-    int64_t carry = 0;
-    int local_max = 0, local_status = 0;
-    for (int base = 0; base < a.B; base += kPlanThreads) {
-        const int b = base + tid;
-        int64_t n = 0;
-        if (b < a.B) {
-            int64_t L = a.lengths[b];
-            if (L < 0 || L > limit) {
-                local_status |= 1;
-                L = 0;
-            }
-            a.len_eff[b] = (int32_t)L;
-            local_max = L > local_max ? (int)L : local_max;
-            n = (L + a.T - 1) / a.T;
+    const int cA = (a.B + kPT - 1) / kPT;
+    const int b0 = min(a.B, tid * cA), b1 = min(a.B, b0 + cA);
+    int sum = 0, mx = 0, st = 0;
+    for (int b = b0; b < b1; ++b) {
+        int L = a.lengths[b];
+        if (L < 0 || (int64_t)L > limit) {
+            st = 1;
+            L = 0;
         }
-        int64_t tot;
-        const int64_t incl = block_inclusive_scan(n, scan_tmp, &tot);
-        if (b < a.B) {
-            tp[b + 1] = (int32_t)(carry + incl);
-            a.tiles_prefix[b + 1] = (int32_t)(carry + incl);
-        }
-        carry += tot;
+        a.len_eff[b] = L;
+        mx = max(mx, L);
+        const int n = (L + a.T - 1) / a.T;
+        tp[b + 1] = n;   // tile count for now; turned into the prefix below
+        sum += n;
     }
-    if (tid == 0)
+    int total;
+    int run = block_excl_scan(sum, scan_lds, &total);
+    for (int b = b0; b < b1; ++b) {
+        run += tp[b + 1];
+        tp[b + 1] = run;
+        a.tiles_prefix[b + 1] = run;
+    }
+    mx = wave_max(mx);
+    st = wave_or(st);
+    if (lane == 0) {
+        red_lds[wave] = mx;
+        red_lds[kPW + wave] = st;
+    }
+    if (tid == 0) {
+        tp[0] = 0;
         a.tiles_prefix[0] = 0;
-    atomicMax(&red_max, local_max);
-    atomicOr(&red_status, local_status);
+    }
     __syncthreads();
-    const int64_t total = carry;   // sum of tiles (same in every thread)
-    const int32_t maxle = red_max;
-    const int32_t status = red_status;
+    int maxle = 0, status = 0;
+#pragma unroll
+    for (int i = 0; i < kPW; ++i) {
+        maxle = max(maxle, red_lds[i]);
+        status |= red_lds[kPW + i];
+    }
     const int nbg = a.B * a.Hkv;
 
     if (a.mode == 1) {
@@ -124,15 +157,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a)
             C = (maxle + S - 1) / S;
             C = (C + gran - 1) / gran * gran;
         }
-        for (int bg = tid; bg <= nbg; bg += kPlanThreads) {
+        for (int bg = tid; bg <= nbg; bg += kPT) {
             a.seg_prefix[bg] = (int32_t)(bg * S);
             if (bg < nbg)
                 a.first_wg[bg] = (int32_t)(bg * S);
         }
         if (tid == 0) {
             const int32_t NB = (int32_t)(nbg * S);
-            const int32_t h[kHeaderInts] = {status, NB, NB, maxle, (int32_t)C, (int32_t)S,
-                                            (int32_t)total, a.T};
+            const int32_t h[kHeaderInts] = {status, NB, NB, maxle, (int32_t)C, (int32_t)S, total, a.T};
             for (int i = 0; i < kHeaderInts; ++i)
                 a.header[i] = h[i];
         }
@@ -140,59 +172,70 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a)
     }
 
     // 2d) dynamic: segments per (b, g) and their prefix
-    const int64_t N = total * a.Hkv;
+    const int64_t N = (int64_t)total * a.Hkv;
     const int64_t We = N < a.W ? N : a.W;
-    carry = 0;
-    for (int base = 0; base < nbg; base += kPlanThreads) {
-        const int bg = base + tid;
-        int64_t segs = 0;
-        if (bg < nbg) {
-            const int b = bg / a.Hkv, g = bg % a.Hkv;
-            const int64_t nb = tp[b + 1] - tp[b];
-            if (nb == 0) {
-                a.first_wg[bg] = -1;
-            } else {
-                const int64_t u0 = (int64_t)tp[b] * a.Hkv + g * nb;
-                const int64_t u1 = u0 + nb - 1;
-                const int64_t w0 = ((u0 + 1) * We - 1) / N;
-                const int64_t w1 = ((u1 + 1) * We - 1) / N;
-                a.first_wg[bg] = (int32_t)w0;
-                segs = w1 - w0 + 1;
-            }
+    const int cB = (nbg + kPT - 1) / kPT;
+    const int g0 = min(nbg, tid * cB), g1 = min(nbg, g0 + cB);
+    int segs = 0;
+    for (int bg = g0; bg < g1; ++bg) {
+        const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+        const int64_t nb = tp[b + 1] - tp[b];
+        if (nb == 0) {
+            a.first_wg[bg] = -1;
+        } else {
+            const int64_t u0 = (int64_t)tp[b] * a.Hkv + g * nb;
+            const int64_t w0 = div_floor((u0 + 1) * We - 1, N);
+            const int64_t w1 = div_floor((u0 + nb) * We - 1, N);
+            a.first_wg[bg] = (int32_t)w0;
+            segs += (int)(w1 - w0 + 1);
         }
-        int64_t tot;
-        const int64_t incl = block_inclusive_scan(segs, scan_tmp, &tot);
-        if (bg < nbg)
-            a.seg_prefix[bg + 1] = (int32_t)(carry + incl);
-        carry += tot;
+    }
+    int nseg;
+    run = block_excl_scan(segs, scan_lds, &nseg);
+    for (int bg = g0; bg < g1; ++bg) {
+        const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+        const int64_t nb = tp[b + 1] - tp[b];
+        if (nb) {
+            const int64_t u0 = (int64_t)tp[b] * a.Hkv + g * nb;
+            run += (int)(div_floor((u0 + nb) * We - 1, N) - div_floor((u0 + 1) * We - 1, N) + 1);
+        }
+        a.seg_prefix[bg + 1] = run;
     }
     if (tid == 0)
         a.seg_prefix[0] = 0;
 
     // 3) workgroup ranges and the request of each range's first unit
-    for (int w = tid; w <= a.W; w += kPlanThreads) {
-        const int64_t begin = (w <= We && We > 0) ? (int64_t)w * N / We : N;
+    const int cC = (a.W + 1 + kPT - 1) / kPT;
+    const int w0 = min(a.W + 1, tid * cC), w1 = min(a.W + 1, w0 + cC);
+    int sb = 0;
+    if (w0 < w1 && We > 0) {
+        // largest b in [0, B) with Hkv * tp[b] <= begin(w0)
+        const int64_t begin = w0 <= We ? div_floor((int64_t)w0 * N, We) : N;
+        int lo = 0, hi = a.B - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if ((int64_t)tp[mid] * a.Hkv <= begin)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        sb = lo;
+    }
+    for (int w = w0; w < w1; ++w) {
+        const int64_t begin = (w <= We && We > 0) ? div_floor((int64_t)w * N, We) : N;
         a.wg_begin[w] = (int32_t)begin;
         if (w < a.W) {
-            int32_t sb = a.B;
             if (w < We) {
-                // largest b in [0, B) with Hkv * tp[b] <= begin
-                int lo = 0, hi = a.B - 1;
-                while (lo < hi) {
-                    const int mid = (lo + hi + 1) >> 1;
-                    if ((int64_t)tp[mid] * a.Hkv <= begin)
-                        lo = mid;
-                    else
-                        hi = mid - 1;
-                }
-                sb = lo;
+                while (sb + 1 < a.B && (int64_t)tp[sb + 1] * a.Hkv <= begin)
+                    ++sb;
+                a.wg_start_b[w] = sb;
+            } else {
+                a.wg_start_b[w] = a.B;
             }
-            a.wg_start_b[w] = sb;
         }
     }
     if (tid == 0) {
-        const int32_t h[kHeaderInts] = {status, (int32_t)N, (int32_t)We, maxle, 0, 0,
-                                        (int32_t)total, a.T};
+        const int32_t h[kHeaderInts] = {status, (int32_t)N, (int32_t)We, maxle, 0, 0, total, a.T};
         for (int i = 0; i < kHeaderInts; ++i)
             a.header[i] = h[i];
     }
@@ -202,7 +245,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a)
 
 hipError_t launch_plan(const PlanArgs &a, hipStream_t st)
 {
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, a);
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPT), 0, st, a);
     return hipGetLastError();
 }
 
