@@ -10,9 +10,12 @@ batch once (2 * Hkv * D * 2 bytes per token) divided by the step time.
 
 Also reported (field "extra"): the skewed batch (1 x 16000 + 63 x 1000
 tokens) under the dynamic plan and under the in-library static split-K at its
-default split count and a split sweep, and the long-tail batch. Those are
-timed per step with HIP events, with a 1 GiB read sweep between steps so that no
-step starts with the previous step's data in the 256 MB Infinity Cache.
+default split count and a split sweep, the long-tail batch, and the 256-step
+continuous-batching trace over an fp8 e4m3 cache (plan rebuilt and timed every
+step). Those are timed per step with HIP events, with a 1 GiB read sweep
+between steps so that no step starts with the previous step's data in the
+256 MB Infinity Cache. The CPU reference is timed on the host as a reported
+baseline ("cpu_baseline").
 
 Prints ONE JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -130,25 +133,108 @@ def per_step_flushed(run, att, steps, warmup, torch, flush):
     return np.array(ts)
 
 
-def cpu_baseline(case, budget_s=20.0):
-    """The CPU reference (fp64 C, OpenMP) on a bounded sample of the same
-    workload: whole requests, taken in index order until the budget is spent."""
+def cpu_baseline(case, budget_s=10.0):
+    """The CPU reference (fp64 C, OpenMP over (request, kv head)) on the same
+    workload: whole passes over all requests, repeated until budget_s seconds
+    of CPU time have been spent (at least one pass)."""
     import oracle
     threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
-    done, tokens, t_total = [], 0, 0.0
-    for b in range(case.B):
+    passes, t_total = 0, 0.0
+    while passes == 0 or t_total < budget_s:
         t0 = time.perf_counter()
-        oracle.decode(case, [b], threads=threads)
-        dt = time.perf_counter() - t0
-        done.append(b)
-        tokens += int(case.lengths[b])
-        t_total += dt
-        if t_total >= budget_s:
-            break
-    nbytes = 2 * case.Hkv * case.D * case.elem_bytes * tokens
+        oracle.decode(case, threads=threads)
+        t_total += time.perf_counter() - t0
+        passes += 1
+    nbytes = case.kv_bytes * passes
     return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(done)} of {case.B} requests ({tokens} tokens, {nbytes / 1e6:.1f} MB of KV), "
-                      f"{t_total:.1f} s, fp64 C with OpenMP over (request, kv head)"}
+            "sample": f"{passes} whole passes over the headline workload ({case.B} requests, "
+                      f"{case.total_tokens} tokens, {case.kv_bytes / 1e6:.1f} MB of KV each) in "
+                      f"{t_total:.1f} s; fp64 C, OpenMP over (request, kv head)"}
+
+
+def trace_leg(torch, L, W, flush, steps=256):
+    """Workload 4: the continuous-batching trace with an fp8 cache. Each step
+    is timed alone (events around attn_plan..attn_combine, so the plan rebuild
+    is included), after a cache flush; host updates and uploads happen between
+    steps, outside the timed region."""
+    from variable_length_kv_amd import workloads as wl
+    from variable_length_kv_amd.trace import DeviceTrace
+    t0 = time.perf_counter()
+    tr = wl.Trace(steps=steps)
+    dt = DeviceTrace(tr)
+    log(f"bench: trace generated in {time.perf_counter() - t0:.1f} s ({tr.num_pages} pages)")
+    shape = L.AttnShape(batch=tr.slots, num_q_heads=tr.Hq, num_kv_heads=tr.Hkv, page_size=tr.P,
+                        num_pages=tr.num_pages, pt_stride=tr.pt_stride, num_wgs=W,
+                        kv_dtype=L.ATTN_KV_FP8_E4M3)
+    att = L.Attention(shape, "cuda:0")
+    out = torch.empty_like(dt.q)
+    lse = torch.empty(tr.slots, tr.Hq, dtype=torch.float32, device="cuda:0")
+    sm = 1.0 / math.sqrt(tr.D)
+
+    def launch(evs=None):
+        if evs:
+            evs[0].record()
+        att.plan(dt.len, dt.pt)
+        if evs:
+            evs[1].record()
+        att.decode(dt.q, dt.k, dt.v, dt.pt, sm, out, lse, dt.ks, dt.vs)
+        if evs:
+            evs[2].record()
+        att.combine(out, lse)
+        if evs:
+            evs[3].record()
+
+    for _ in range(5):
+        launch()
+    torch.cuda.synchronize()
+    per, kvb = [], []
+    while True:
+        flush.sum()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        launch(evs)
+        torch.cuda.synchronize()
+        per.append([evs[j].elapsed_time(evs[j + 1]) for j in range(3)])
+        kvb.append(2 * tr.Hkv * tr.D * int(np.asarray(tr.lengths, np.int64).sum()))
+        if dt.step == steps - 1:
+            break
+        dt.advance()
+    per = np.array(per) * 1e3   # us
+    tot = per.sum(axis=1)
+    kvb = np.array(kvb, np.float64)
+    gbs = kvb.sum() / (tot.sum() * 1e-6) / 1e9
+    return {"steps": steps, "kv_gb_mean": round(float(kvb.mean()) / 1e9, 4),
+            "us_per_step_median": round(float(np.median(tot)), 2),
+            "us_per_step_p10": round(float(np.percentile(tot, 10)), 2),
+            "us_per_step_p90": round(float(np.percentile(tot, 90)), 2),
+            "us_per_step_p99": round(float(np.percentile(tot, 99)), 2),
+            "us_per_step_mean": round(float(tot.mean()), 2),
+            "plan_us_median": round(float(np.median(per[:, 0])), 2),
+            "decode_us_median": round(float(np.median(per[:, 1])), 2),
+            "combine_us_median": round(float(np.median(per[:, 2])), 2),
+            "effective_gbs": round(gbs, 2), "pct_hbm": round(100 * gbs / HBM_PEAK_GBS, 2)}
+
+
+def traffic_probe(torch, L, W, reps=3):
+    """Launches for rocprofv3 --pmc runs: a plain 1 GiB device copy (the
+    counter scale), then the headline decode step, each `reps` times, with a
+    cache flush before each launch."""
+    from variable_length_kv_amd import workloads as wl
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        flush.sum()
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    c1 = wl.config_case(1)
+    r = Runner(c1, torch, L, W)
+    att = r.attention(L.ATTN_DYNAMIC)
+    for _ in range(reps):
+        flush.sum()
+        r.step(att)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": src.numel() * 4, "decode_kv_bytes": c1.kv_bytes, "reps": reps}),
+          flush=True)
 
 
 def traffic_entry(decode_ms_avg):
@@ -170,7 +256,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--wgs-per-cu", type=int, default=2)
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
-    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--trace-steps", type=int, default=256)
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="only the launches that the rocprofv3 --pmc runs measure")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would run its own "
@@ -184,6 +273,9 @@ def main():
     L.load()
     cus = L.attn_device_cu_count(0)
     W = args.wgs_per_cu * cus
+    if args.traffic_probe:
+        traffic_probe(torch, L, W)
+        return
 
     # ---- headline: uniform-mixed batch, dynamic plan ------------------------
     t0 = time.perf_counter()
@@ -269,7 +361,10 @@ def main():
             log(f"bench: {label}: {json.dumps(entry)}")
             del r
             torch.cuda.empty_cache()
+        extra["trace_fp8"] = trace_leg(torch, L, W, flush, args.trace_steps)
+        log(f"bench: trace_fp8: {json.dumps(extra['trace_fp8'])}")
         del flush
+        torch.cuda.empty_cache()
         result["extra"] = extra
 
     # ---- CPU baseline (the oracle, bounded sample of the headline workload) ---

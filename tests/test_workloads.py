@@ -52,3 +52,38 @@ def test_fp8_codes_saturate_and_scale():
     k = c.k_cache.view(torch.float8_e4m3fn).float()
     assert torch.isfinite(k).all() and k.abs().max() <= 448
     assert c.k_scale.shape == (2, 2) and (c.k_scale > 0).all()
+
+
+def _small_trace():
+    return wl.Trace(steps=40, slots=6, Hq=8, Hkv=2, P=16, seed=1, p_finish=0.15, new_lo=5, new_hi=70,
+                    init_lo=10, init_hi=120)
+
+
+def test_trace_host_state_is_consistent():
+    tr = _small_trace()
+    while tr.step < tr.steps - 1:
+        tr.advance()
+        P = tr.P
+        used = []
+        for b in range(tr.slots):
+            n = -(-int(tr.lengths[b]) // P)
+            assert (tr.page_table[b, :n] >= 0).all() and (tr.page_table[b, n:] == -1).all()
+            used += tr.page_table[b, :n].tolist()
+        # no page is owned twice, and owned pages are never on the free list
+        assert len(used) == len(set(used))
+        assert not (set(used) & set(tr.free))
+        assert len(used) + len(tr.free) == tr.num_pages
+
+
+def test_device_mirror_tracks_the_host_trace():
+    from variable_length_kv_amd.trace import DeviceTrace
+    tr = _small_trace()
+    dt = DeviceTrace(tr, "cpu")
+    assert dt.k.data_ptr() != tr.k_cache.data_ptr()
+    for _ in range(tr.steps - 1):
+        dt.advance()
+        assert torch.equal(dt.k, tr.k_cache) and torch.equal(dt.v, tr.v_cache)
+        assert torch.equal(dt.ks, tr.k_scale) and torch.equal(dt.vs, tr.v_scale)
+        assert np.array_equal(dt.pt.numpy(), tr.page_table)
+        assert np.array_equal(dt.len.numpy(), tr.lengths)
+        assert torch.equal(dt.q, tr.q)

@@ -1,0 +1,55 @@
+"""Device mirror of the continuous-batching trace (``workloads.Trace``).
+
+The host trace owns the fp8 page pool, the page table, the lengths and the
+per-(slot, kv-head) scales; after each ``advance()`` this class patches the
+device copies with exactly what changed (the appended token rows, the pages
+written for replacement requests) and re-uploads the small arrays (lengths,
+page table, scales, queries). Copies are plain host-to-device transfers made
+between steps, outside any timed region. No attention arithmetic lives here.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import workloads as wl
+
+
+class DeviceTrace:
+    def __init__(self, trace: wl.Trace, device="cuda:0"):
+        self.tr = trace
+        self.dev = torch.device(device)
+        def up(t):
+            return t.to(self.dev, copy=True)
+        self.k = up(trace.k_cache)
+        self.v = up(trace.v_cache)
+        self.ks = up(trace.k_scale)
+        self.vs = up(trace.v_scale)
+        self.pt = up(torch.from_numpy(np.ascontiguousarray(trace.page_table)))
+        self.len = up(torch.from_numpy(np.ascontiguousarray(trace.lengths, np.int32)))
+        self.q = up(trace.q)
+
+    @property
+    def step(self) -> int:
+        return self.tr.step
+
+    def advance(self):
+        """Host transition step -> step+1, then patch the device copies."""
+        tr = self.tr
+        patch = tr.advance()
+        pages, slots = patch["rows"]
+        if len(pages):
+            dp, ds = pages.to(self.dev), slots.to(self.dev)
+            self.k[dp, :, ds] = tr.k_cache[pages, :, slots].to(self.dev)
+            self.v[dp, :, ds] = tr.v_cache[pages, :, slots].to(self.dev)
+        whole = patch["pages"]
+        if len(whole):
+            dw = whole.to(self.dev)
+            self.k[dw] = tr.k_cache[whole].to(self.dev)
+            self.v[dw] = tr.v_cache[whole].to(self.dev)
+        self.ks.copy_(tr.k_scale)
+        self.vs.copy_(tr.v_scale)
+        self.pt.copy_(torch.from_numpy(np.ascontiguousarray(tr.page_table)))
+        self.len.copy_(torch.from_numpy(np.ascontiguousarray(tr.lengths, np.int32)))
+        self.q.copy_(tr.q)
+        return patch
