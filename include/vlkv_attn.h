@@ -166,6 +166,37 @@ int attn_combine(const attn_shape *shape, const void *workspace, size_t workspac
                  void *out, float *lse, void *stream);
 
 /*
+ * Prepare a workspace for attn_step: clears the status word and the per-(request,
+ * kv head) arrival counters (one small kernel on `stream`). Call it once after
+ * allocating the workspace (and after any shape change that reuses it); every
+ * attn_step leaves the counters at zero again, so no per-step clearing is needed.
+ */
+int attn_workspace_init(const attn_shape *shape, void *workspace, size_t workspace_bytes,
+                        void *stream);
+
+/*
+ * One decode step in a single kernel launch: the same plan, decode and merge as
+ * attn_plan + attn_decode + attn_combine, with identical results up to the order
+ * in which split partials are summed. Every workgroup derives its own unit range
+ * of the current tile plan from `lengths` (the per-step rebuild of the article's
+ * tile-to-CTA mapping [Tencent HPC lands in SGLang, challenging default
+ * inference kernels, sec. "Why Tencent HPC matters for online model serving"]),
+ * and the last workgroup to finish a (request, kv head) pair that is split over
+ * several workgroups merges the pair's partials by log-sum-exp weighting.
+ *   lengths    (device) int32 [B], current context length of each request
+ *   other arguments as in attn_decode; shape->mode selects the dynamic plan or
+ *   the static split-K.
+ * The workspace must have been prepared by attn_workspace_init. The status word
+ * is sticky: bits set by any step stay set until attn_workspace_init or
+ * attn_plan rewrites it. Two attn_step calls on one workspace must not overlap
+ * (same stream, or ordered).
+ */
+int attn_step(const attn_shape *shape, const void *q, const void *k_cache, const void *v_cache,
+              const float *k_scale, const float *v_scale, const int32_t *page_table,
+              const int32_t *lengths, float sm_scale, void *workspace, size_t workspace_bytes,
+              void *out, float *lse, void *stream);
+
+/*
  * Copy the status word of the last plan/decode on this workspace into *flags
  * (host pointer). SYNCHRONISES `stream`; meant for tests and debugging, not
  * for the per-step path.

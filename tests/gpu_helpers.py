@@ -60,17 +60,20 @@ def shape_for(case, mode=L.ATTN_DYNAMIC, T=64, W=None, S=0):
 
 
 def run(case, mode=L.ATTN_DYNAMIC, T=64, W=None, S=0, t=None, poison=True, lengths=None,
-        page_table=None):
-    """One plan+decode+combine step. Returns (out float64 [B,Hq,D], lse float64 [B,Hq], att)."""
+        page_table=None, fused=False, att=None):
+    """One decode step: attn_plan + attn_decode + attn_combine, or the
+    single-launch attn_step if ``fused``. Returns (out float64 [B,Hq,D],
+    lse float64 [B,Hq], att)."""
     if t is None:
         t = device_inputs(case, poison)
-    shape = shape_for(case, mode, T, W, S)
-    att = L.Attention(shape, dev())
+    if att is None:
+        att = L.Attention(shape_for(case, mode, T, W, S), dev())
     out = torch.full_like(t["q"], float("nan"))
     lse = torch.full((case.B, case.Hq), float("nan"), dtype=torch.float32, device=dev())
-    att.step(t["q"], t["k"], t["v"], t["pt"] if page_table is None else page_table,
-             t["len"] if lengths is None else lengths, case.sm_scale, out, lse,
-             k_scale=t["ks"], v_scale=t["vs"])
+    step = att.fused_step if fused else att.step
+    step(t["q"], t["k"], t["v"], t["pt"] if page_table is None else page_table,
+         t["len"] if lengths is None else lengths, case.sm_scale, out, lse,
+         k_scale=t["ks"], v_scale=t["vs"])
     torch.cuda.synchronize()
     return out.double().cpu().numpy(), lse.double().cpu().numpy(), att
 

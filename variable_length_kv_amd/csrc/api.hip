@@ -1,5 +1,6 @@
 // C ABI of libvlkv_attn.so (declared in include/vlkv_attn.h): host-side
-// argument checks, the workspace layout, and the three per-step launches.
+// argument checks, the workspace layout, the three per-step launches and the
+// single-launch step.
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -111,7 +112,9 @@ WsLayout ws_layout(const Shape &s)
         return at;
     };
     const int64_t nbg = (int64_t)s.B * s.Hkv;
-    L.max_slots = s.mode == ATTN_STATIC ? nbg * s.S : nbg + s.W;
+    // dynamic: at most W_eff + B*Hkv segments with attn_plan's slots, and two
+    // slots per workgroup (its first and last segment) in the single launch
+    L.max_slots = s.mode == ATTN_STATIC ? nbg * s.S : nbg + 2 * (int64_t)s.W;
     L.header = take(sizeof(int32_t) * kHeaderInts);
     L.len_eff = take(sizeof(int32_t) * s.B);
     L.tiles_prefix = take(sizeof(int32_t) * (s.B + 1));
@@ -119,6 +122,7 @@ WsLayout ws_layout(const Shape &s)
     L.first_wg = take(sizeof(int32_t) * nbg);
     L.wg_begin = take(sizeof(int32_t) * (s.W + 1));
     L.wg_start_b = take(sizeof(int32_t) * s.W);
+    L.counters = take(sizeof(int32_t) * nbg);
     L.part_lse = take(sizeof(float) * L.max_slots * s.G);
     L.part_o = take(sizeof(float) * L.max_slots * s.G * s.D);
     L.total = off;
@@ -251,6 +255,8 @@ int attn_decode(const attn_shape *shape, const void *q, const void *k_cache, con
     if ((rc = check_ws(s, workspace, workspace_bytes, &L)) != ATTN_OK)
         return rc;
     DecodeArgs a;
+    a.lengths = nullptr;
+    a.counters = nullptr;
     a.q = static_cast<const uint16_t *>(q);
     a.k = static_cast<const uint8_t *>(k_cache);
     a.v = static_cast<const uint8_t *>(v_cache);
@@ -277,9 +283,12 @@ int attn_decode(const attn_shape *shape, const void *q, const void *k_cache, con
     a.pt_stride = s.pt_stride;
     a.blocks_per_tile = s.T / kBlockTokens;
     a.S = s.S;
+    a.T = s.T;
+    a.W = s.W;
     a.scale_log2 = sm_scale * 1.4426950408889634f;
     const int grid = s.mode == ATTN_STATIC ? s.B * s.Hkv * s.S : s.W;
-    const hipError_t e = launch_decode(a, s.mode, s.kv_fp8, grid, static_cast<hipStream_t>(stream));
+    const hipError_t e = launch_decode(a, s.mode == ATTN_STATIC ? SRC_STATIC : SRC_DYNAMIC, s.kv_fp8, grid,
+                                       static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return hip_fail(e, "decode launch");
     return ok();
@@ -315,6 +324,77 @@ int attn_combine(const attn_shape *shape, const void *workspace, size_t workspac
     const hipError_t e = launch_combine(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return hip_fail(e, "combine launch");
+    return ok();
+}
+
+int attn_workspace_init(const attn_shape *shape, void *workspace, size_t workspace_bytes, void *stream)
+{
+    Shape s;
+    WsLayout L;
+    int rc = check(shape, &s);
+    if (rc != ATTN_OK)
+        return rc;
+    if ((rc = check_ws(s, workspace, workspace_bytes, &L)) != ATTN_OK)
+        return rc;
+    const hipError_t e = launch_ws_init(at<int32_t>(workspace, L.header), at<int32_t>(workspace, L.counters),
+                                        s.B * s.Hkv, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "workspace init launch");
+    return ok();
+}
+
+int attn_step(const attn_shape *shape, const void *q, const void *k_cache, const void *v_cache,
+              const float *k_scale, const float *v_scale, const int32_t *page_table,
+              const int32_t *lengths, float sm_scale, void *workspace, size_t workspace_bytes,
+              void *out, float *lse, void *stream)
+{
+    Shape s;
+    WsLayout L;
+    int rc = check(shape, &s);
+    if (rc != ATTN_OK)
+        return rc;
+    if (!q || !k_cache || !v_cache || !page_table || !lengths || !out)
+        return fail(ATTN_ERR_INVALID_ARG, "q, k_cache, v_cache, page_table, lengths and out must be non-NULL");
+    if (s.kv_fp8 && (!k_scale || !v_scale))
+        return fail(ATTN_ERR_INVALID_ARG, "fp8 cache needs k_scale and v_scale");
+    if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY)
+        return fail(ATTN_ERR_INVALID_ARG, "sm_scale is not finite");
+    if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
+         reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(out)) % 16)
+        return fail(ATTN_ERR_INVALID_ARG, "q, caches and out must be 16-byte aligned");
+    if ((rc = check_ws(s, workspace, workspace_bytes, &L)) != ATTN_OK)
+        return rc;
+    DecodeArgs a{};
+    a.lengths = lengths;
+    a.counters = at<int32_t>(workspace, L.counters);
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint8_t *>(k_cache);
+    a.v = static_cast<const uint8_t *>(v_cache);
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.page_table = page_table;
+    a.header = at<int32_t>(workspace, L.header);
+    a.part_o = at<float>(workspace, L.part_o);
+    a.part_lse = at<float>(workspace, L.part_lse);
+    a.out = static_cast<uint16_t *>(out);
+    a.lse = lse;
+    a.B = s.B;
+    a.Hq = s.Hq;
+    a.Hkv = s.Hkv;
+    a.G = s.G;
+    a.P = s.P;
+    a.num_pages = s.num_pages;
+    a.pt_stride = s.pt_stride;
+    a.blocks_per_tile = s.T / kBlockTokens;
+    a.S = s.S;
+    a.T = s.T;
+    a.W = s.W;
+    a.scale_log2 = sm_scale * 1.4426950408889634f;
+    const int grid = s.mode == ATTN_STATIC ? s.B * s.Hkv * s.S : s.W;
+    const hipError_t e = launch_decode(a, s.mode == ATTN_STATIC ? SRC_FUSED_STATIC : SRC_FUSED_DYNAMIC,
+                                       s.kv_fp8, grid, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "step launch");
     return ok();
 }
 

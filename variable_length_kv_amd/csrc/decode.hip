@@ -5,8 +5,11 @@
 // current load, and split results are merged ("split-k"); the static split-k is
 // the comparison point [Tencent HPC lands in SGLang, challenging default
 // inference kernels, sec. "Why Tencent HPC matters for online model serving"].
-// Both variants here share one per-block body and differ only in where a
-// workgroup's sequence of (request, kv head, block range) segments comes from.
+// All variants here share one per-block body and differ only in where a
+// workgroup's sequence of (request, kv head, block range) segments comes from:
+// the plan arrays attn_plan wrote, or (single launch) the lengths themselves,
+// from which every workgroup derives its own unit range; then the last
+// workgroup to finish a split (request, kv head) pair merges its partials.
 //
 // Workgroup = 4 wave64s. A 64-token block of one (request b, kv head g) is split
 // into four 16-token slices, one per wave; every wave walks the same sequence of
@@ -32,6 +35,7 @@
 //     which is the A operand (V^T) of the 16x16x16 bf16 MFMA. The product is
 //     exact (one nonzero term), so it also widens fp8 codes to bf16 for free.
 //   * O^T (128 dims x 16 heads) += V^T P^T with 8 MFMAs into 32 fp32 registers.
+#include "vlkv_device.hpp"
 #include "vlkv_internal.hpp"
 
 namespace vlkv {
@@ -49,10 +53,10 @@ constexpr int kLdsRow = kHeadDim + 4;  // padded fp32 row of the merge buffer
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Read-only data of the step (plan arrays, page table, scales) is read through
-// the constant address space: wave-uniform addresses then become scalar loads,
-// which are counted apart from the K/V vector loads, so waiting for a page id
-// never waits for K/V data still in flight.
+// Read-only data of the step (plan arrays, lengths, page table, scales) is read
+// through the constant address space: wave-uniform addresses then become scalar
+// loads, which are counted apart from the K/V vector loads, so waiting for a
+// page id never waits for K/V data still in flight.
 template <typename T>
 __device__ __forceinline__ T ldc(const T *p, size_t i)
 {
@@ -90,6 +94,14 @@ __device__ __forceinline__ int out_dim(int mb, int c)
     return 16 * mb + c;
 }
 
+// Validated length of request b as the planner defines it: L_b if
+// 0 <= L_b <= pt_stride * P, else 0.
+__device__ __forceinline__ int len_valid(const DecodeArgs *a, int b)
+{
+    const int L = ldc(a->lengths, b);
+    return (L < 0 || (int64_t)L > (int64_t)a->pt_stride * a->P) ? 0 : L;
+}
+
 // Registers of one in-flight slice (fp8 uses k[0..1], v[0..1]).
 struct Slot {
     u32x4 k[4];
@@ -107,17 +119,38 @@ struct Meta {
     int last;    // last block of its segment
     int slot;    // partial slot
     int direct;  // write the final output directly
+    int nseg;    // single launch: segments of the pair (arrivals before its merge)
+    int wfirst;  // single launch, dynamic: workgroup of the pair's first segment
+    int first_off;  // single launch, dynamic: slot offset of that first segment
     float ksc, vsc;
 };
 
-// Walks a workgroup's blocks in order. Dynamic: the contiguous unit range of
-// the plan; static: the one (b, g, split) of this workgroup.
-template <int MODE>
+// Walks a workgroup's blocks in order. SRC_DYNAMIC / SRC_FUSED_DYNAMIC: the
+// contiguous unit range of the plan; SRC_STATIC / SRC_FUSED_STATIC: the one
+// (b, g, split) of this workgroup.
+template <int SRC>
 struct Walker {
+    static constexpr bool kFused = SRC == SRC_FUSED_DYNAMIC || SRC == SRC_FUSED_STATIC;
+    static constexpr bool kDyn = SRC == SRC_DYNAMIC || SRC == SRC_FUSED_DYNAMIC;
+
     const DecodeArgs *a;
     int w, wave;
     int b, g, blk, blk0, blk_end, L, nt, units_left, done;
-    int slot, direct;
+    int slot, direct, nseg, wfirst, first_off;
+    // single launch, dynamic
+    int tpb;                 // tiles before request b
+    int first_seg;           // the next segment entered is the workgroup's first
+    int64_t N, We, u_beg, u_end;
+
+    __device__ int64_t owner(int64_t u) const { return div_floor((u + 1) * We - 1, N); }
+    __device__ int64_t begin_of(int64_t ww) const { return div_floor(ww * N, We); }
+
+    __device__ int tiles_of(int bb) const
+    {
+        return kFused ? (len_valid(a, bb) + a->T - 1) / a->T
+                      : ldc(a->tiles_prefix, bb + 1) - ldc(a->tiles_prefix, bb);
+    }
+    __device__ int length_of(int bb) const { return kFused ? len_valid(a, bb) : ldc(a->len_eff, bb); }
 
     __device__ void enter_segment(int ta, int tb)
     {
@@ -126,26 +159,70 @@ struct Walker {
         const int nblk = (L + kBlockTokens - 1) / kBlockTokens;
         blk_end = min(tb * R, nblk);
         const int bg = b * a->Hkv + g;
-        const int s0 = ldc(a->seg_prefix, bg);
-        const int s1 = ldc(a->seg_prefix, bg + 1);
-        slot = s0 + (w - ldc(a->first_wg, bg));
-        direct = (s1 - s0) == 1;
+        if (SRC == SRC_DYNAMIC) {
+            const int s0 = ldc(a->seg_prefix, bg);
+            const int s1 = ldc(a->seg_prefix, bg + 1);
+            slot = s0 + (w - ldc(a->first_wg, bg));
+            direct = (s1 - s0) == 1;
+        } else {
+            // slot 2w for the workgroup's first segment, 2w+1 for its last; a
+            // segment that is neither covers its whole pair and is direct
+            const int64_t pu0 = (int64_t)tpb * a->Hkv + (int64_t)g * nt;
+            direct = pu0 >= u_beg && pu0 + nt <= u_end;
+            slot = 2 * w + (first_seg ? 0 : 1);
+            first_seg = 0;
+            if (!direct) {
+                const int64_t wf = owner(pu0);
+                wfirst = (int)wf;
+                nseg = (int)(owner(pu0 + nt - 1) - wf + 1);
+                first_off = begin_of(wf) < pu0 ? 1 : 0;
+            }
+        }
     }
 
-    __device__ void init(const DecodeArgs *args, int wg, int wv)
+    // lds_tp: tiles prefix (single launch, dynamic only)
+    __device__ void init(const DecodeArgs *args, int wg, int wv, const int32_t *lds_tp, int64_t N_, int64_t We_,
+                         int chunk)
     {
         a = args;
         w = wg;
         wave = wv;
         done = 0;
-        if (MODE == 0) {
-            const int u0 = ldc(a->wg_begin, w);
-            const int u1 = ldc(a->wg_begin, w + 1);
-            b = ldc(a->wg_start_b, w);
-            const int tp0 = ldc(a->tiles_prefix, b);
-            nt = ldc(a->tiles_prefix, b + 1) - tp0;
-            L = ldc(a->len_eff, b);
-            const int rem = u0 - tp0 * a->Hkv;
+        nseg = 1;
+        wfirst = 0;
+        first_off = 0;
+        if (kDyn) {
+            int u0, u1;
+            if (SRC == SRC_DYNAMIC) {
+                u0 = ldc(a->wg_begin, w);
+                u1 = ldc(a->wg_begin, w + 1);
+                b = ldc(a->wg_start_b, w);
+                tpb = ldc(a->tiles_prefix, b);
+                nt = ldc(a->tiles_prefix, b + 1) - tpb;
+            } else {
+                N = N_;
+                We = We_;
+                u_beg = begin_of(w);
+                u_end = begin_of(w + 1);
+                u0 = (int)u_beg;
+                u1 = (int)u_end;
+                // largest b in [0, B) with Hkv * tp[b] <= u0: the request of unit u0
+                int lo = 0, hi = a->B - 1;
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    const int t = __builtin_amdgcn_readfirstlane(lds_tp[mid]);
+                    if ((int64_t)t * a->Hkv <= u0)
+                        lo = mid;
+                    else
+                        hi = mid - 1;
+                }
+                b = lo;
+                tpb = __builtin_amdgcn_readfirstlane(lds_tp[b]);
+                nt = __builtin_amdgcn_readfirstlane(lds_tp[b + 1]) - tpb;
+                first_seg = 1;
+            }
+            L = length_of(b);
+            const int rem = u0 - tpb * a->Hkv;
             g = rem / nt;
             const int t = rem - g * nt;
             const int take = min(nt - t, u1 - u0);
@@ -156,12 +233,13 @@ struct Walker {
             const int bg = w / S, s = w - bg * S;
             b = bg / a->Hkv;
             g = bg - b * a->Hkv;
-            L = ldc(a->len_eff, b);
-            const int C = ldc(a->header, H_CHUNK);
+            L = length_of(b);
+            const int C = SRC == SRC_STATIC ? ldc(a->header, H_CHUNK) : chunk;
             const int lo = s * C, hi = min(lo + C, L);
             units_left = 0;
             slot = w;
             direct = S == 1;
+            nseg = S;
             blk = blk0 = lo / kBlockTokens;
             if (hi > lo) {
                 blk_end = (hi + kBlockTokens - 1) / kBlockTokens;
@@ -174,11 +252,22 @@ struct Walker {
         }
     }
 
+    // Step to the next request that has tiles.
+    __device__ void next_request()
+    {
+        do {
+            tpb += nt;
+            ++b;
+            nt = tiles_of(b);
+        } while (nt == 0);
+        L = length_of(b);
+    }
+
     // Number of blocks this workgroup will process (a scalar walk over its
     // segments; the walker itself is not advanced).
     __device__ int count_blocks() const
     {
-        if (MODE != 0)
+        if (!kDyn)
             return blk_end - blk;
         int n = blk_end - blk;
         int bb = b, gg = g, ntt = nt, LL = L, left = units_left;
@@ -188,9 +277,9 @@ struct Walker {
                 gg = 0;
                 do {
                     ++bb;
-                    ntt = ldc(a->tiles_prefix, bb + 1) - ldc(a->tiles_prefix, bb);
+                    ntt = tiles_of(bb);
                 } while (ntt == 0);
-                LL = ldc(a->len_eff, bb);
+                LL = length_of(bb);
             }
             const int take = min(ntt, left);
             left -= take;
@@ -213,21 +302,20 @@ struct Walker {
         m.last = !done && blk + 1 == blk_end;
         m.slot = slot;
         m.direct = direct;
+        m.nseg = nseg;
+        m.wfirst = wfirst;
+        m.first_off = first_off;
         m.ksc = 1.f;
         m.vsc = 1.f;
         if (done)
             return m;
         ++blk;
         if (blk == blk_end) {
-            if (MODE == 0 && units_left > 0) {
+            if (kDyn && units_left > 0) {
                 ++g;
                 if (g == a->Hkv) {
                     g = 0;
-                    do {
-                        ++b;
-                        nt = ldc(a->tiles_prefix, b + 1) - ldc(a->tiles_prefix, b);
-                    } while (nt == 0);
-                    L = ldc(a->len_eff, b);
+                    next_request();
                 }
                 const int take = min(nt, units_left);
                 units_left -= take;
@@ -240,26 +328,176 @@ struct Walker {
     }
 };
 
-template <int MODE, int KVFP8>
+// Loads and stores of the partials exchanged between workgroups inside one
+// launch. Relaxed atomics at agent scope are coherent across the chip's L2
+// caches (they are performed at the device's coherence point), so no L2-wide
+// writeback or invalidation is needed; ordering comes from waiting for the
+// stores to complete before the arrival counter moves.
+__device__ __forceinline__ void store_coherent(float *p, float x)
+{
+    __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float *p)
+{
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Merge n partial results (o normalised, lse in base 2) of one (request, kv
+// head) pair into the bf16 output and the natural-log lse. slot_of(s) gives the
+// slot of the s-th partial. Run by all threads of a workgroup. COHERENT reads
+// the partials with agent-scope loads (partials written in the same launch).
+template <bool COHERENT, typename SlotOf>
+__device__ __forceinline__ void merge_partials(const float *part_o, const float *part_lse, int n, SlotOf slot_of,
+                                               int G, int Hq, int b, int g, uint16_t *out, float *lse)
+{
+    constexpr int D = kHeadDim;
+    constexpr int kBatch = 4;   // partials whose loads are issued together
+    auto ld = [](const float *p) { return COHERENT ? load_coherent(p) : *p; };
+    for (int idx = threadIdx.x; idx < G * 32; idx += kDecodeThreads) {
+        const int h = idx >> 5, d4 = (idx & 31) * 4;
+        // running merge: M the largest lse so far, den = sum 2^(lse_s - M),
+        // o = sum 2^(lse_s - M) o_s
+        float M = -INFINITY, den = 0.f;
+        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+        for (int s0 = 0; s0 < n; s0 += kBatch) {
+            float ls[kBatch];
+            f32x4 xs[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const size_t sl = (size_t)slot_of(s0 + j < n ? s0 + j : s0) * G + h;
+                ls[j] = ld(part_lse + sl);
+                const float *po = part_o + sl * D + d4;
+                if (COHERENT)
+                    xs[j] = f32x4{ld(po), ld(po + 1), ld(po + 2), ld(po + 3)};
+                else
+                    xs[j] = *reinterpret_cast<const f32x4 *>(po);
+            }
+            float Mb = M;
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j)
+                if (s0 + j < n)
+                    Mb = fmaxf(Mb, ls[j]);
+            if (Mb == -INFINITY)
+                continue;   // every partial so far is empty
+            const float r = fast_exp2(M - Mb);   // 0 when M is -inf
+            den *= r;
+            o *= r;
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                if (s0 + j < n) {
+                    const float e = fast_exp2(ls[j] - Mb);
+                    den += e;
+                    o += e * xs[j];
+                }
+            }
+            M = Mb;
+        }
+        float lse2 = -INFINITY;
+        if (M != -INFINITY) {
+            o *= 1.f / den;
+            lse2 = M + log2f(den);
+        } else {
+            o = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        const size_t hq = (size_t)b * Hq + (size_t)g * G + h;
+        *reinterpret_cast<bf16x4 *>(out + hq * D + d4) = __builtin_convertvector(o, bf16x4);
+        if (lse && d4 == 0)
+            lse[hq] = lse2 * kLn2;
+    }
+}
+
+struct DecodeLds {
+    union {
+        float acc[kWaves][kMaxGroup][kLdsRow];  // per-wave states at a segment's end
+        int32_t tp[kMaxBatch + 1];              // single launch: tiles prefix (prologue only)
+    };
+    float m[kWaves][kMaxGroup];
+    float l[kWaves][kMaxGroup];
+    float e[kWaves][kMaxGroup];
+    int red[2 * kWaves];
+    int flag;
+};
+
+template <int SRC, int KVFP8>
 __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
 {
+    constexpr bool kFused = SRC == SRC_FUSED_DYNAMIC || SRC == SRC_FUSED_STATIC;
     const int w = blockIdx.x;
-    if (MODE == 0 && w >= ldc(a.header, H_WEFF))
+    if (SRC == SRC_DYNAMIC && w >= ldc(a.header, H_WEFF))
         return;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int row = lane & 15;   // MFMA row / column within a 16x16 tile
     const int grp = lane >> 4;   // MFMA row group
 
-    __shared__ __attribute__((aligned(16))) float lds_acc[kWaves][kMaxGroup][kLdsRow];
-    __shared__ float lds_m[kWaves][kMaxGroup];
-    __shared__ float lds_l[kWaves][kMaxGroup];
-    __shared__ float lds_e[kWaves][kMaxGroup];
+    __shared__ __attribute__((aligned(16))) DecodeLds lds;
 
     const int G = a.G;
     constexpr int D = kHeadDim;
     constexpr int EB = KVFP8 ? 1 : 2;             // bytes per cached element
     const size_t page_head_bytes = (size_t)a.P * D * EB;
+
+    // ---- single launch: this workgroup's share of the plan ---------------
+    int64_t N = 0, We = 0;
+    int chunk = 0;
+    if (kFused) {
+        const int tid = threadIdx.x;
+        const int cA = (a.B + kDecodeThreads - 1) / kDecodeThreads;
+        const int b0 = min(a.B, tid * cA), b1 = min(a.B, b0 + cA);
+        int sum = 0, mx = 0, bad = 0;
+        const int64_t limit = (int64_t)a.pt_stride * a.P;
+        for (int bb = b0; bb < b1; ++bb) {
+            const int raw = a.lengths[bb];
+            const int Lb = (raw < 0 || (int64_t)raw > limit) ? 0 : raw;
+            bad |= Lb != raw;
+            mx = max(mx, Lb);
+            const int n = (Lb + a.T - 1) / a.T;
+            if (SRC == SRC_FUSED_DYNAMIC)
+                lds.tp[bb + 1] = n;
+            sum += n;
+        }
+        int maxle, bits;
+        block_max_or<kDecodeThreads>(mx, bad, lds.red, &maxle, &bits);
+        maxle = __builtin_amdgcn_readfirstlane(maxle);
+        bits = __builtin_amdgcn_readfirstlane(bits);
+        if (bits && w == 0 && tid == 0)
+            atomicOr(reinterpret_cast<unsigned *>(a.header + H_STATUS), 1u);
+        if (SRC == SRC_FUSED_DYNAMIC) {
+            int total;
+            int run = block_excl_scan<kDecodeThreads>(sum, lds.red, &total);
+            total = __builtin_amdgcn_readfirstlane(total);
+            for (int bb = b0; bb < b1; ++bb) {
+                run += lds.tp[bb + 1];
+                lds.tp[bb + 1] = run;
+            }
+            if (tid == 0)
+                lds.tp[0] = 0;
+            // requests without tiles: o = 0, lse = -inf (spread over the grid)
+            for (int bb = w; bb < a.B; bb += gridDim.x) {
+                if (len_valid(&a, bb) != 0)
+                    continue;
+                for (int idx = tid; idx < a.Hq * 32; idx += kDecodeThreads) {
+                    const int h = idx >> 5, d4 = (idx & 31) * 4;
+                    const size_t hq = (size_t)bb * a.Hq + h;
+                    *reinterpret_cast<bf16x4 *>(a.out + hq * D + d4) = bf16x4{0, 0, 0, 0};
+                    if (a.lse && d4 == 0)
+                        a.lse[hq] = -INFINITY;
+                }
+            }
+            N = (int64_t)total * a.Hkv;
+            We = N < a.W ? N : a.W;
+            __syncthreads();   // the tiles prefix is complete
+            if (w >= We)
+                return;
+        } else {
+            const int64_t S = a.S;
+            const int64_t gran = (int64_t)a.P / gcd64(a.P, a.T) * a.T;
+            if (maxle > 0) {
+                int64_t C = (maxle + S - 1) / S;
+                chunk = (int)((C + gran - 1) / gran * gran);
+            }
+        }
+    }
 
     // 0/1 selection matrices for the in-register V transpose: B operand, lane
     // (n = row, grp) element j stands for k = 8*grp + j; Sel_s[k][n] = (k == n + 16 s)
@@ -277,8 +515,10 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
         sel8[s] = bits;
     }
 
-    Walker<MODE> wk;
-    wk.init(&a, w, wave);
+    Walker<SRC> wk;
+    wk.init(&a, w, wave, lds.tp, N, We, chunk);
+    if (SRC == SRC_FUSED_DYNAMIC)
+        __syncthreads();   // every wave has read the tiles prefix; lds.acc may now be written
 
     // per-wave softmax state, head = row. m_run is uniform over the 4 row
     // groups; l_run is this lane's partial sum, reduced at segment end.
@@ -357,18 +597,18 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
         const float e_tot = xsum4(e_run);
         if (row < G) {
             if (grp == 0) {
-                lds_m[wave][row] = m_run;
-                lds_l[wave][row] = l_tot;
-                lds_e[wave][row] = e_tot;
+                lds.m[wave][row] = m_run;
+                lds.l[wave][row] = l_tot;
+                lds.e[wave][row] = e_tot;
             }
 #pragma unroll
             for (int mb = 0; mb < 8; ++mb) {
                 if (KVFP8) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        lds_acc[wave][row][out_dim<1>(mb, 4 * grp + i)] = acc[mb][i];
+                        lds.acc[wave][row][out_dim<1>(mb, 4 * grp + i)] = acc[mb][i];
                 } else {
-                    *reinterpret_cast<f32x4 *>(&lds_acc[wave][row][16 * mb + 4 * grp]) = acc[mb];
+                    *reinterpret_cast<f32x4 *>(&lds.acc[wave][row][16 * mb + 4 * grp]) = acc[mb];
                 }
             }
         }
@@ -379,17 +619,17 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
             float M = -INFINITY;
 #pragma unroll
             for (int v = 0; v < kWaves; ++v)
-                M = fmaxf(M, lds_m[v][h]);
+                M = fmaxf(M, lds.m[v][h]);
             f32x4 o = {0.f, 0.f, 0.f, 0.f};
             float lse2 = -INFINITY;
             if (M != -INFINITY) {
                 float den = 0.f, ex = 0.f;
 #pragma unroll
                 for (int v = 0; v < kWaves; ++v) {
-                    const float e = fast_exp2(lds_m[v][h] - M);
-                    den += e * lds_l[v][h];
-                    ex += e * lds_e[v][h];
-                    const f32x4 x = *reinterpret_cast<const f32x4 *>(&lds_acc[v][h][d4]);
+                    const float e = fast_exp2(lds.m[v][h] - M);
+                    den += e * lds.l[v][h];
+                    ex += e * lds.e[v][h];
+                    const f32x4 x = *reinterpret_cast<const f32x4 *>(&lds.acc[v][h][d4]);
                     o += e * x;
                 }
                 const float r = vsc_run / den;
@@ -402,10 +642,47 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
                 *reinterpret_cast<bf16x4 *>(a.out + hq * D + d4) = ob;
                 if (a.lse && d4 == 0)
                     a.lse[hq] = lse2 * kLn2;
+            } else if (kFused) {
+                float *po = a.part_o + ((size_t)mt.slot * G + h) * D + d4;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    store_coherent(po + i, o[i]);
+                if (d4 == 0)
+                    store_coherent(a.part_lse + (size_t)mt.slot * G + h, lse2);
             } else {
                 *reinterpret_cast<f32x4 *>(a.part_o + ((size_t)mt.slot * G + h) * D + d4) = o;
                 if (d4 == 0)
                     a.part_lse[(size_t)mt.slot * G + h] = lse2;
+            }
+        }
+        if (kFused && !mt.direct) {
+            // Arrival: each wave waits for its coherent partial stores to
+            // complete before the barrier, so they are visible device-wide before
+            // the counter moves; the last of the pair's nseg workgroups merges
+            // the pair's partials with coherent loads.
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            const int bg = mt.b * a.Hkv + mt.g;
+            if (tid == 0) {
+                const int old = __hip_atomic_fetch_add(a.counters + bg, 1, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+                const int last = old == mt.nseg - 1;
+                if (last)   // every arrival of this step is in: leave the counter at 0
+                    __hip_atomic_store(a.counters + bg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                lds.flag = last;
+            }
+            __syncthreads();
+            if (lds.flag) {
+                if (SRC == SRC_FUSED_DYNAMIC) {
+                    const int wf = mt.wfirst, off = mt.first_off;
+                    merge_partials<true>(a.part_o, a.part_lse, mt.nseg,
+                                         [=](int s) { return 2 * (wf + s) + (s == 0 ? off : 0); },
+                                         G, a.Hq, mt.b, mt.g, a.out, a.lse);
+                } else {
+                    const int s0 = bg * a.S;
+                    merge_partials<true>(a.part_o, a.part_lse, mt.nseg, [=](int s) { return s0 + s; },
+                                         G, a.Hq, mt.b, mt.g, a.out, a.lse);
+                }
             }
         }
         __syncthreads();
@@ -519,6 +796,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
         compute(s1, m1);
         issue(s1, m1);
     }
+
     if (bad_page && lane == 0)
         atomicOr(reinterpret_cast<unsigned *>(a.header + H_STATUS), 2u);
 }
@@ -539,47 +817,39 @@ __global__ __launch_bounds__(kDecodeThreads) void combine_kernel(CombineArgs a)
     }
     if (n == 1)
         return;
-    const int G = a.G;
-    constexpr int D = kHeadDim;
-    for (int idx = threadIdx.x; idx < G * 32; idx += kDecodeThreads) {
-        const int h = idx >> 5, d4 = (idx & 31) * 4;
-        float M = -INFINITY;
-        for (int s = 0; s < n; ++s)
-            M = fmaxf(M, a.part_lse[(size_t)(s0 + s) * G + h]);
-        f32x4 o = {0.f, 0.f, 0.f, 0.f};
-        float lse2 = -INFINITY;
-        if (M != -INFINITY) {
-            float den = 0.f;
-            for (int s = 0; s < n; ++s) {
-                const size_t sl = (size_t)(s0 + s) * G + h;
-                const float e = fast_exp2(a.part_lse[sl] - M);
-                den += e;
-                o += e * *reinterpret_cast<const f32x4 *>(a.part_o + sl * D + d4);
-            }
-            o *= 1.f / den;
-            lse2 = M + log2f(den);
-        }
-        const size_t hq = (size_t)b * a.Hq + (size_t)g * G + h;
-        *reinterpret_cast<bf16x4 *>(a.out + hq * D + d4) = __builtin_convertvector(o, bf16x4);
-        if (a.lse && d4 == 0)
-            a.lse[hq] = lse2 * kLn2;
-    }
+    merge_partials<false>(a.part_o, a.part_lse, n, [=](int s) { return s0 + s; }, a.G, a.Hq, b, g, a.out,
+                          a.lse);
+}
+
+// Clears the status word and the arrival counters of a workspace.
+__global__ __launch_bounds__(256) void ws_init_kernel(int32_t *header, int32_t *counters, int n)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < kHeaderInts)
+        header[i] = 0;
+    if (i < n)
+        counters[i] = 0;
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs &a, int mode, int kv_fp8, int grid, hipStream_t st)
+hipError_t launch_decode(const DecodeArgs &a, int src, int kv_fp8, int grid, hipStream_t st)
 {
     if (grid <= 0)
         return hipSuccess;
-    if (mode == 0 && !kv_fp8)
-        hipLaunchKernelGGL((decode_kernel<0, 0>), dim3(grid), dim3(kDecodeThreads), 0, st, a);
-    else if (mode == 0)
-        hipLaunchKernelGGL((decode_kernel<0, 1>), dim3(grid), dim3(kDecodeThreads), 0, st, a);
-    else if (!kv_fp8)
-        hipLaunchKernelGGL((decode_kernel<1, 0>), dim3(grid), dim3(kDecodeThreads), 0, st, a);
-    else
-        hipLaunchKernelGGL((decode_kernel<1, 1>), dim3(grid), dim3(kDecodeThreads), 0, st, a);
+#define VLKV_LAUNCH(S, F) hipLaunchKernelGGL((decode_kernel<S, F>), dim3(grid), dim3(kDecodeThreads), 0, st, a)
+    switch (src * 2 + (kv_fp8 ? 1 : 0)) {
+    case 0: VLKV_LAUNCH(SRC_DYNAMIC, 0); break;
+    case 1: VLKV_LAUNCH(SRC_DYNAMIC, 1); break;
+    case 2: VLKV_LAUNCH(SRC_STATIC, 0); break;
+    case 3: VLKV_LAUNCH(SRC_STATIC, 1); break;
+    case 4: VLKV_LAUNCH(SRC_FUSED_DYNAMIC, 0); break;
+    case 5: VLKV_LAUNCH(SRC_FUSED_DYNAMIC, 1); break;
+    case 6: VLKV_LAUNCH(SRC_FUSED_STATIC, 0); break;
+    case 7: VLKV_LAUNCH(SRC_FUSED_STATIC, 1); break;
+    default: return hipErrorInvalidValue;
+    }
+#undef VLKV_LAUNCH
     return hipGetLastError();
 }
 
@@ -589,6 +859,13 @@ hipError_t launch_combine(const CombineArgs &a, hipStream_t st)
     if (grid <= 0)
         return hipSuccess;
     hipLaunchKernelGGL(combine_kernel, dim3(grid), dim3(kDecodeThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_ws_init(int32_t *header, int32_t *counters, int n_counters, hipStream_t st)
+{
+    const int n = n_counters > kHeaderInts ? n_counters : kHeaderInts;
+    hipLaunchKernelGGL(ws_init_kernel, dim3((n + 255) / 256), dim3(256), 0, st, header, counters, n_counters);
     return hipGetLastError();
 }
 

@@ -20,6 +20,7 @@
 // The work is O(B*Hkv + W) and latency-bound: each thread owns a contiguous
 // chunk of every array, so a prefix sum is one serial pass per thread, one
 // wave scan and one exchange of 4 wave totals through LDS.
+#include "vlkv_device.hpp"
 #include "vlkv_internal.hpp"
 
 namespace vlkv {
@@ -27,76 +28,6 @@ namespace {
 
 constexpr int kPT = 256;  // planner threads
 constexpr int kPW = kPT / 64;
-
-__device__ __forceinline__ int wave_incl_scan(int x)
-{
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off, 64);
-        if (lane >= off)
-            x += y;
-    }
-    return x;
-}
-
-__device__ __forceinline__ int wave_max(int x)
-{
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        x = max(x, __shfl_xor(x, off, 64));
-    return x;
-}
-
-__device__ __forceinline__ int wave_or(int x)
-{
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        x |= __shfl_xor(x, off, 64);
-    return x;
-}
-
-// Exclusive prefix of one int per thread over the workgroup (in thread order);
-// *total receives the sum over all threads.
-__device__ int block_excl_scan(int v, int *lds, int *total)
-{
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int incl = wave_incl_scan(v);
-    if (lane == 63)
-        lds[wave] = incl;
-    __syncthreads();
-    int before = 0, all = 0;
-#pragma unroll
-    for (int i = 0; i < kPW; ++i) {
-        const int t = lds[i];
-        before += i < wave ? t : 0;
-        all += t;
-    }
-    __syncthreads();  // lds is reused by the next scan
-    *total = all;
-    return before + incl - v;
-}
-
-// floor(x / d) for 0 <= x < 2^53, d > 0: double estimate, exact correction.
-__device__ __forceinline__ int64_t div_floor(int64_t x, int64_t d)
-{
-    int64_t q = (int64_t)((double)x / (double)d);
-    if (q * d > x)
-        --q;
-    else if ((q + 1) * d <= x)
-        ++q;
-    return q;
-}
-
-__device__ __forceinline__ int64_t gcd64(int64_t a, int64_t b)
-{
-    while (b) {
-        const int64_t t = a % b;
-        a = b;
-        b = t;
-    }
-    return a;
-}
 
 __global__ __launch_bounds__(kPT) void plan_kernel(PlanArgs a)
 {
@@ -123,7 +54,7 @@ __global__ __launch_bounds__(kPT) void plan_kernel(PlanArgs a)
         sum += n;
     }
     int total;
-    int run = block_excl_scan(sum, scan_lds, &total);
+    int run = block_excl_scan<kPT>(sum, scan_lds, &total);
     for (int b = b0; b < b1; ++b) {
         run += tp[b + 1];
         tp[b + 1] = run;
@@ -191,7 +122,7 @@ __global__ __launch_bounds__(kPT) void plan_kernel(PlanArgs a)
         }
     }
     int nseg;
-    run = block_excl_scan(segs, scan_lds, &nseg);
+    run = block_excl_scan<kPT>(segs, scan_lds, &nseg);
     for (int bg = g0; bg < g1; ++bg) {
         const int b = bg / a.Hkv, g = bg - b * a.Hkv;
         const int64_t nb = tp[b + 1] - tp[b];

@@ -1,0 +1,109 @@
+// Device helpers shared by the planner and the decode kernels: wave and
+// workgroup scans/reductions over wave64, and exact integer division used by
+// the tile partition. Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vlkv {
+
+__device__ __forceinline__ int wave_incl_scan(int x)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off)
+            x += y;
+    }
+    return x;
+}
+
+__device__ __forceinline__ int wave_max(int x)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        x = max(x, __shfl_xor(x, off, 64));
+    return x;
+}
+
+__device__ __forceinline__ int wave_or(int x)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        x |= __shfl_xor(x, off, 64);
+    return x;
+}
+
+// Exclusive prefix of one int per thread over a workgroup of NT threads (in
+// thread order); *total receives the sum over all threads. `lds` holds NT/64
+// ints. Every thread of the workgroup must call it.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int *lds, int *total)
+{
+    constexpr int NW = NT / 64;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int incl = wave_incl_scan(v);
+    if (lane == 63)
+        lds[wave] = incl;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const int t = lds[i];
+        before += i < wave ? t : 0;
+        all += t;
+    }
+    __syncthreads();  // lds is reused by the next call
+    *total = all;
+    return before + incl - v;
+}
+
+// Max and OR of one int per thread over a workgroup of NT threads; `lds` holds
+// 2*NT/64 ints.
+template <int NT>
+__device__ __forceinline__ void block_max_or(int mx, int bits, int *lds, int *mx_out, int *bits_out)
+{
+    constexpr int NW = NT / 64;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    mx = wave_max(mx);
+    bits = wave_or(bits);
+    if (lane == 0) {
+        lds[wave] = mx;
+        lds[NW + wave] = bits;
+    }
+    __syncthreads();
+    int m = 0, o = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        m = max(m, lds[i]);
+        o |= lds[NW + i];
+    }
+    __syncthreads();
+    *mx_out = m;
+    *bits_out = o;
+}
+
+// floor(x / d) for 0 <= x < 2^53, d > 0: double estimate, exact correction.
+__device__ __forceinline__ int64_t div_floor(int64_t x, int64_t d)
+{
+    int64_t q = (int64_t)((double)x / (double)d);
+    if (q * d > x)
+        --q;
+    else if ((q + 1) * d <= x)
+        ++q;
+    return q;
+}
+
+__device__ __forceinline__ int64_t gcd64(int64_t a, int64_t b)
+{
+    while (b) {
+        const int64_t t = a % b;
+        a = b;
+        b = t;
+    }
+    return a;
+}
+
+}  // namespace vlkv

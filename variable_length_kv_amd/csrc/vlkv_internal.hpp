@@ -14,7 +14,6 @@ constexpr int kSlice = 16;         // tokens per wave per 64-token block
 constexpr int kBlockTokens = 64;   // kWaves * kSlice
 constexpr int kDecodeThreads = 256;
 constexpr int kMaxGroup = 16;      // query heads per kv head (one MFMA column block)
-constexpr int kPlanThreads = 1024;
 constexpr int kMaxBatch = 8192;    // planner keeps the tile prefix in LDS
 constexpr int kHeaderInts = 8;
 
@@ -25,8 +24,16 @@ enum : int { H_STATUS = 0, H_UNITS = 1, H_WEFF = 2, H_MAXLEN = 3, H_CHUNK = 4, H
 // Byte offsets of the workspace regions (all 256-B aligned).
 struct WsLayout {
     size_t header, len_eff, tiles_prefix, seg_prefix, first_wg, wg_begin, wg_start_b;
-    size_t part_lse, part_o, total;
+    size_t counters, part_lse, part_o, total;
     int64_t max_slots;
+};
+
+// Where a decode workgroup's sequence of segments comes from.
+enum PlanSrc : int {
+    SRC_DYNAMIC = 0,        // plan arrays written by attn_plan (dynamic mode)
+    SRC_STATIC = 1,         // plan arrays written by attn_plan (static mode)
+    SRC_FUSED_DYNAMIC = 2,  // single launch: each workgroup derives its range from the lengths
+    SRC_FUSED_STATIC = 3,   // single launch, static split-K
 };
 
 struct Shape {
@@ -42,6 +49,8 @@ struct PlanArgs {
 };
 
 struct DecodeArgs {
+    const int32_t *lengths;    // raw per-request lengths (single-launch sources only)
+    int32_t *counters;         // [B*Hkv] arrival counters (single-launch sources only)
     const uint16_t *q;         // [B][Hq][D] bf16 bits
     const uint8_t *k;          // cache base (bytes)
     const uint8_t *v;
@@ -52,7 +61,7 @@ struct DecodeArgs {
     float *part_o, *part_lse;
     uint16_t *out;             // [B][Hq][D] bf16 bits
     float *lse;                // [B][Hq] or null
-    int B, Hq, Hkv, G, P, num_pages, pt_stride, blocks_per_tile, S;
+    int B, Hq, Hkv, G, P, num_pages, pt_stride, blocks_per_tile, S, T, W;
     float scale_log2;          // sm_scale * log2(e)
 };
 
@@ -65,7 +74,8 @@ struct CombineArgs {
 };
 
 hipError_t launch_plan(const PlanArgs &a, hipStream_t st);
-hipError_t launch_decode(const DecodeArgs &a, int mode, int kv_fp8, int grid, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs &a, int src, int kv_fp8, int grid, hipStream_t st);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t st);
+hipError_t launch_ws_init(int32_t *header, int32_t *counters, int n_counters, hipStream_t st);
 
 }  // namespace vlkv

@@ -24,7 +24,7 @@ ATTN_STATUS_BAD_LENGTH, ATTN_STATUS_BAD_PAGE = 1, 2
 
 EXPORTED = ("attn_check_shape", "attn_workspace_bytes", "attn_static_splits", "attn_device_cu_count",
             "attn_plan", "attn_decode", "attn_combine", "attn_get_status", "attn_read_plan",
-            "attn_last_error")
+            "attn_workspace_init", "attn_step", "attn_last_error")
 
 
 class AttnError(RuntimeError):
@@ -83,6 +83,8 @@ def load():
         "attn_combine": (i32, [SP, P, sz, P, P, P]),
         "attn_get_status": (i32, [P, P, P]),
         "attn_read_plan": (i32, [SP, P, P, P, P, P, P, P, P, P]),
+        "attn_workspace_init": (i32, [SP, P, sz, P]),
+        "attn_step": (i32, [SP, P, P, P, P, P, P, P, ctypes.c_float, P, sz, P, P, P]),
         "attn_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sigs.items():
@@ -160,6 +162,18 @@ def attn_combine(shape, workspace, out, lse=None, stream=None) -> None:
                                _ptr(out), _ptr(lse), _stream(stream)))
 
 
+def attn_workspace_init(shape, workspace, stream=None) -> None:
+    _check(load().attn_workspace_init(_shape(shape), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(stream)))
+
+
+def attn_step(shape, q, k_cache, v_cache, k_scale, v_scale, page_table, lengths, sm_scale, workspace, out,
+              lse=None, stream=None) -> None:
+    _check(load().attn_step(_shape(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                            _ptr(page_table), _ptr(lengths), float(sm_scale), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(stream)))
+
+
 def attn_get_status(workspace, stream=None) -> int:
     out = ctypes.c_uint32()
     _check(load().attn_get_status(_ptr(workspace), ctypes.byref(out), _stream(stream)))
@@ -185,15 +199,23 @@ class Attention:
     """One decode-attention configuration with its own workspace.
 
     ``step`` enqueues attn_plan, attn_decode and attn_combine on the current
-    stream. The workspace is a torch uint8 tensor (device memory only).
+    stream; ``fused_step`` enqueues the single-launch attn_step. The workspace
+    is a torch uint8 tensor (device memory only), prepared by
+    attn_workspace_init when the object is made.
     """
 
-    def __init__(self, shape: AttnShape, device="cuda"):
+    def __init__(self, shape: AttnShape, device="cuda", stream=None):
         self.shape = shape
         n = attn_workspace_bytes(shape)
         self.workspace = torch.empty(n + 256, dtype=torch.uint8, device=device)
         off = (-self.workspace.data_ptr()) % 256
         self.workspace = self.workspace[off:off + n]
+        attn_workspace_init(shape, self.workspace, stream)
+
+    def fused_step(self, q, k_cache, v_cache, page_table, lengths, sm_scale, out, lse=None, k_scale=None,
+                   v_scale=None, stream=None):
+        attn_step(self.shape, q, k_cache, v_cache, k_scale, v_scale, page_table, lengths, sm_scale,
+                  self.workspace, out, lse, stream)
 
     def plan(self, lengths, page_table, stream=None):
         attn_plan(self.shape, lengths, page_table, self.workspace, stream)
