@@ -202,10 +202,19 @@ def stats(ts_ms, kv_bytes):
             "pct_hbm": round(100 * kv_bytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
 
 
-def batch_leg(cid, torch, L, wl, W, flush, static_sweep=False):
+def pick_wgs(args, L, cus, lengths, Hkv):
+    """Workgroups of the dynamic plan: --wgs-per-cu if given, else the
+    library's occupancy suggestion for these lengths."""
+    if args.wgs_per_cu > 0:
+        return args.wgs_per_cu * cus
+    return L.suggest_num_wgs(cus, lengths, Hkv)
+
+
+def batch_leg(cid, torch, L, wl, W_of, flush, static_sweep=False):
     c = wl.config_case(cid)
+    W = W_of(c.lengths, c.Hkv)
     r = Runner(c, torch, L, W)
-    entry = {"kv_gb": round(c.kv_bytes / 1e9, 4), "tokens": c.total_tokens}
+    entry = {"kv_gb": round(c.kv_bytes / 1e9, 4), "tokens": c.total_tokens, "num_wgs": W}
     a = r.attention(L.ATTN_DYNAMIC)
     entry["dynamic"] = stats(per_step_flushed(r, a, 30, 5, torch, flush, True), c.kv_bytes)
     entry["dynamic_three_launch"] = stats(per_step_flushed(r, a, 30, 5, torch, flush, False), c.kv_bytes)
@@ -240,7 +249,7 @@ def batch_leg(cid, torch, L, wl, W, flush, static_sweep=False):
     return entry
 
 
-def trace_leg(torch, L, W, flush, steps=256):
+def trace_leg(torch, L, W_of, flush, steps=256):
     """Workload 4: the continuous-batching trace with an fp8 cache. Each step is
     timed alone after a cache flush: the single-launch step (its plan is built
     inside the kernel) and the three-launch step (attn_plan included). Host
@@ -251,6 +260,7 @@ def trace_leg(torch, L, W, flush, steps=256):
     tr = wl.Trace(steps=steps)
     dt = DeviceTrace(tr)
     log(f"bench: trace generated in {time.perf_counter() - t0:.1f} s ({tr.num_pages} pages)")
+    W = W_of(tr.lengths, tr.Hkv)
     shape = L.AttnShape(batch=tr.slots, num_q_heads=tr.Hq, num_kv_heads=tr.Hkv, page_size=tr.P,
                         num_pages=tr.num_pages, pt_stride=tr.pt_stride, num_wgs=W,
                         kv_dtype=L.ATTN_KV_FP8_E4M3)
@@ -307,7 +317,8 @@ def trace_leg(torch, L, W, flush, steps=256):
                 "us_per_step_mean": round(float(t.mean()), 2),
                 "effective_gbs": round(gbs, 2), "pct_hbm": round(100 * gbs / HBM_PEAK_GBS, 2)}
 
-    out_d = {"steps": steps, "kv_gb_mean": round(float(kvb.mean()) / 1e9, 4), "single_launch": summary(tf),
+    out_d = {"steps": steps, "num_wgs": W, "kv_gb_mean": round(float(kvb.mean()) / 1e9, 4),
+             "single_launch": summary(tf),
              "three_launch": summary(t3s)}
     out_d["three_launch"].update({"plan_us_median": round(float(np.median(t3[:, 0])), 2),
                                   "decode_us_median": round(float(np.median(t3[:, 1])), 2),
@@ -357,7 +368,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--wgs-per-cu", type=int, default=2)
+    ap.add_argument("--wgs-per-cu", type=int, default=0,
+                    help="workgroups per CU of the dynamic plan (0: the library's suggestion per workload)")
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--trace-steps", type=int, default=256)
@@ -375,9 +387,12 @@ def main():
     from variable_length_kv_amd import workloads as wl
     L.load()
     cus = L.attn_device_cu_count(0)
-    W = args.wgs_per_cu * cus
+
+    def W_of(lengths, Hkv):
+        return pick_wgs(args, L, cus, lengths, Hkv)
+
     if args.traffic_probe:
-        traffic_probe(torch, L, W)
+        traffic_probe(torch, L, W_of(wl.config_lengths(1), 8))
         return
 
     # ---- headline: uniform-mixed batch, dynamic plan ------------------------
@@ -385,6 +400,7 @@ def main():
     c1 = wl.config_case(1)
     log(f"bench: workload 1 generated in {time.perf_counter() - t0:.1f} s "
         f"({c1.kv_bytes / 1e9:.3f} GB of KV, {c1.total_tokens} tokens)")
+    W = W_of(c1.lengths, c1.Hkv)
     r1 = Runner(c1, torch, L, W)
     att = r1.attention(L.ATTN_DYNAMIC)
     ms, per_f = timed_fused(r1, att, args.steps, args.warmup, torch)
@@ -433,11 +449,11 @@ def main():
     if not args.no_extra:
         extra = {}
         flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
-        extra["skewed"] = batch_leg(2, torch, L, wl, W, flush, static_sweep=True)
+        extra["skewed"] = batch_leg(2, torch, L, wl, W_of, flush, static_sweep=True)
         log(f"bench: skewed: {json.dumps(extra['skewed'])}")
-        extra["long_tail"] = batch_leg(3, torch, L, wl, W, flush)
+        extra["long_tail"] = batch_leg(3, torch, L, wl, W_of, flush)
         log(f"bench: long_tail: {json.dumps(extra['long_tail'])}")
-        extra["trace_fp8"] = trace_leg(torch, L, W, flush, args.trace_steps)
+        extra["trace_fp8"] = trace_leg(torch, L, W_of, flush, args.trace_steps)
         log(f"bench: trace_fp8: {json.dumps(extra['trace_fp8'])}")
         del flush
         torch.cuda.empty_cache()

@@ -100,3 +100,12 @@ def test_null_arguments_rejected_before_launch():
     assert b"scale" in lib.attn_last_error()
     assert lib.attn_combine(ctypes.byref(s), ws, ctypes.c_size_t(1 << 30), None, None, None) == L.ATTN_ERR_INVALID_ARG
     assert lib.attn_get_status(None, None, None) == L.ATTN_ERR_INVALID_ARG
+
+
+def test_suggested_workgroup_count():
+    # two per compute unit unless that leaves fewer than 32 tiles per workgroup
+    assert L.suggest_num_wgs(256, [16000] + [1000] * 63, 8) == 256     # 10,064 tiles
+    assert L.suggest_num_wgs(256, [8900] * 32, 8) == 512               # 35,840 tiles
+    assert L.suggest_num_wgs(4, [0, -5], 1) == 4
+    assert L.suggest_num_wgs(2, [64 * 32 * 4], 1) == 4                 # exactly 32 tiles per workgroup
+    assert L.suggest_num_wgs(2, [64 * 32 * 4 - 64], 1) == 2

@@ -435,6 +435,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
     const int G = a.G;
     constexpr int D = kHeadDim;
     constexpr int EB = KVFP8 ? 1 : 2;             // bytes per cached element
+    constexpr int kSlots = 2;                      // slices in flight per wave
     const size_t page_head_bytes = (size_t)a.P * D * EB;
 
     // ---- single launch: this workgroup's share of the plan ---------------
@@ -782,19 +783,23 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
             finish(mt);
     };
 
-    // ---- software pipeline: two slices in flight per wave ---------------
-    // A counted loop (the block count is known from the plan) with both slots
-    // handled in every iteration; a trailing invalid block does nothing.
+    // ---- software pipeline: kSlots slices in flight per wave --------------
+    // A counted loop (the block count is known from the plan) with every slot
+    // handled in each iteration; trailing invalid blocks do nothing. (Three or
+    // four slots measured slower on gfx950 for both cache types: more registers,
+    // no more useful bytes in flight.)
     const int nblk = wk.count_blocks();
-    Slot s0, s1;
-    Meta m0, m1;
-    issue(s0, m0);
-    issue(s1, m1);
-    for (int it = 0; it < nblk; it += 2) {
-        compute(s0, m0);
-        issue(s0, m0);
-        compute(s1, m1);
-        issue(s1, m1);
+    Slot sl[kSlots];
+    Meta mt[kSlots];
+#pragma unroll
+    for (int i = 0; i < kSlots; ++i)
+        issue(sl[i], mt[i]);
+    for (int it = 0; it < nblk; it += kSlots) {
+#pragma unroll
+        for (int i = 0; i < kSlots; ++i) {
+            compute(sl[i], mt[i]);
+            issue(sl[i], mt[i]);
+        }
     }
 
     if (bad_page && lane == 0)

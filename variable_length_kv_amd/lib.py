@@ -138,6 +138,17 @@ def attn_static_splits(shape) -> int:
     return int(load().attn_static_splits(_shape(shape)))
 
 
+def suggest_num_wgs(cus: int, lengths, num_kv_heads: int, tile_tokens: int = 64, min_units: int = 32) -> int:
+    """Workgroup count for the dynamic plan: two per compute unit (two waves per
+    SIMD hide load latency best on large batches), or one per compute unit when
+    two would leave fewer than ``min_units`` tiles per workgroup, where the fixed
+    per-workgroup costs (plan prologue, segment merges) would dominate."""
+    import numpy as np
+    L = np.asarray(lengths, np.int64)
+    units = int(((np.maximum(L, 0) + tile_tokens - 1) // tile_tokens).sum()) * num_kv_heads
+    return 2 * cus if units >= 2 * cus * min_units else cus
+
+
 def attn_device_cu_count(device: int = 0) -> int:
     out = ctypes.c_int32()
     _check(load().attn_device_cu_count(int(device), ctypes.byref(out)))
