@@ -47,9 +47,12 @@ typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
 typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
+typedef float f32x2 __attribute__((__vector_size__(2 * sizeof(float))));
+typedef short s16x4 __attribute__((__vector_size__(4 * sizeof(short))));
 
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kLdsRow = kHeadDim + 4;  // padded fp32 row of the merge buffer
+constexpr float kLazy = 8.f;           // lazy-rescale threshold (log2 units)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -61,6 +64,25 @@ template <typename T>
 __device__ __forceinline__ T ldc(const T *p, size_t i)
 {
     return ((const __attribute__((address_space(4))) T *)(p))[i];
+}
+
+// Four fp32 values rounded to bf16 (nearest even) and packed as an MFMA
+// operand. Converting in pairs keeps one v_cvt_pk_bf16_f32 per two values;
+// converting the whole vector into an MFMA operand lowers to one convert per
+// value plus byte permutes.
+__device__ __forceinline__ s16x4 pack_bf16x4(f32x4 x)
+{
+    const bf16x2 lo = __builtin_convertvector((f32x2){x[0], x[1]}, bf16x2);
+    const bf16x2 hi = __builtin_convertvector((f32x2){x[2], x[3]}, bf16x2);
+    return __builtin_bit_cast(s16x4, (u32x2){__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)});
+}
+
+// The bf16 values of a packed operand, widened back to fp32 (exact).
+__device__ __forceinline__ f32x4 unpack_bf16x4(s16x4 v)
+{
+    const u32x2 w = __builtin_bit_cast(u32x2, v);
+    return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u), __uint_as_float(w[1] << 16),
+                 __uint_as_float(w[1] & 0xffff0000u)};
 }
 
 // max / sum over lanes l, l^16, l^32, l^48 (the 4 row groups of an MFMA tile)
@@ -536,6 +558,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
         qreg[i] = u32x4{0u, 0u, 0u, 0u};
 
     int bad_page = 0;
+    // this lane's byte offset inside a 16-row slice: row (token) and 16-byte column group
+    const uint32_t lane_off = (uint32_t)row * (D * EB) + 16u * grp;
 
     // ---- loads of one block into a slot ---------------------------------
     // K/V loads are issued for every slot, also past the end of the work or
@@ -561,34 +585,36 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
                 mt.vsc = ldc(a.v_scale, (size_t)mt.b * a.Hkv + mt.g);
             }
         }
-        size_t off = (size_t)mt.g * page_head_bytes + (size_t)row * (D * EB);  // page 0
+        // The slab address is wave-uniform (scalar registers); each lane adds its
+        // fixed 32-bit offset, so the loads take the scalar-base form and no
+        // 64-bit address arithmetic runs per lane.
+        size_t slab = (size_t)mt.g * page_head_bytes;   // page 0 of kv head g
         if (mt.valid && mt.nv > 0) {
             const int page = ldc(a.page_table, (size_t)mt.b * a.pt_stride + mt.tok0 / a.P);
             if (page < 0 || page >= a.num_pages) {
                 bad_page = 1;   // reported once at the end of the kernel
                 mt.nv = 0;
             } else {
-                off = ((size_t)page * a.Hkv + mt.g) * page_head_bytes +
-                      (size_t)(mt.tok0 % a.P + row) * (D * EB);
+                slab = ((size_t)page * a.Hkv + mt.g) * page_head_bytes + (size_t)(mt.tok0 % a.P) * (D * EB);
             }
         }
         if (!mt.valid)
-            off = (size_t)row * (D * EB);
-        const uint8_t *kp = a.k + off;
-        const uint8_t *vp = a.v + off;
+            slab = 0;
+        const uint8_t *kp = a.k + slab;
+        const uint8_t *vp = a.v + slab;
         if (KVFP8) {
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
-                s.k[p] = *reinterpret_cast<const u32x4 *>(kp + 16 * grp + 64 * p);
-                s.v[p] = *reinterpret_cast<const u32x4 *>(vp + 16 * grp + 64 * p);
+                s.k[p] = *reinterpret_cast<const u32x4 *>(kp + lane_off + 64 * p);
+                s.v[p] = *reinterpret_cast<const u32x4 *>(vp + lane_off + 64 * p);
             }
         } else {
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
-                s.k[kk] = *reinterpret_cast<const u32x4 *>(kp + 64 * kk + 16 * grp);
+                s.k[kk] = *reinterpret_cast<const u32x4 *>(kp + lane_off + 64 * kk);
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
-                s.v[kk] = *reinterpret_cast<const u32x4 *>(vp + 64 * kk + 16 * grp);
+                s.v[kk] = *reinterpret_cast<const u32x4 *>(vp + lane_off + 64 * kk);
         }
     };
 
@@ -691,14 +717,13 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
 
     // ---- math of one block ----------------------------------------------
     auto compute = [&](Slot &s, const Meta &mt) {
-        // Every register of the slot is consumed on every path (q through a
-        // select, K/V by the math, which runs even for an empty slice and then
-        // contributes nothing), so the compiler's load-wait bookkeeping never
-        // sees a load whose registers are reloaded without being waited for.
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            qreg[kk] = mt.first ? (row < G ? s.q[kk] : u32x4{0u, 0u, 0u, 0u}) : qreg[kk];
+        // K/V registers are consumed on every path (the math runs even for an
+        // empty slice and then contributes nothing); q only at a segment's
+        // first block, which is the only block that loads it.
         if (mt.first) {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                qreg[kk] = row < G ? s.q[kk] : u32x4{0u, 0u, 0u, 0u};
             m_run = -INFINITY;
             l_run = 0.f;
             e_run = 0.f;
@@ -729,31 +754,41 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
                     st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, s.k[kk]),
                                                                  __builtin_bit_cast(bf16x8, qreg[kk]), st, 0, 0, 0);
             }
-            float mx = -INFINITY;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float x = st[i] * sc;
-                if (4 * grp + i >= mt.nv)
-                    x = -INFINITY;
-                st[i] = x;
-                mx = fmaxf(mx, x);
+            for (int i = 0; i < 4; ++i)
+                st[i] *= sc;
+            if (mt.nv < kSlice) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    st[i] = 4 * grp + i >= mt.nv ? -INFINITY : st[i];
             }
+            float mx = fmaxf(fmaxf(st[0], st[1]), fmaxf(st[2], st[3]));
             mx = xmax4(mx);
-            const float m_new = fmaxf(m_run, mx);
-            const float m_use = m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = fast_exp2(m_run - m_use);
+            // Lazy rescaling: the reference maximum m_run only moves (and the
+            // running sums are rescaled) when a head's scores exceed it by more
+            // than kLazy (log2 units). Weights 2^(s - m_run) then stay <= 2^kLazy,
+            // exact in fp32 and bf16 alike, and every later step uses the same
+            // reference, so the result is unchanged while most slices skip the
+            // 34 multiplies of a rescale.
+            if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy) != 0) {
+                const float m_new = fmaxf(m_run, mx);
+                const float alpha = fast_exp2(m_run - m_new);
+                l_run *= alpha;
+                e_run *= alpha;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    acc[i] *= alpha;
+                m_run = m_new;
+            }
+            const float m_use = m_run == -INFINITY ? 0.f : m_run;
             f32x4 p;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 p[i] = fast_exp2(st[i] - m_use);
-            const bf16x4 pb = __builtin_convertvector(p, bf16x4);
-            const f32x4 pr = __builtin_convertvector(pb, f32x4);
-            l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-            e_run = e_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-            m_run = m_new;
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                acc[i] *= alpha;
+            const s16x4 pb = pack_bf16x4(p);
+            const f32x4 pr = unpack_bf16x4(pb);
+            l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+            e_run += (p[0] + p[1]) + (p[2] + p[3]);
             // rows past the length may hold anything (NaN): zero them
             if (mt.nv < kSlice && row >= mt.nv) {
 #pragma unroll
@@ -774,8 +809,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
                         t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, s.v[kk]),
                                                                     sel16[ss], zero, 0, 0, 0);
                     }
-                    const bf16x4 vt = __builtin_convertvector(t, bf16x4);
-                    acc[2 * kk + ss] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pb, acc[2 * kk + ss], 0, 0, 0);
+                    acc[2 * kk + ss] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pack_bf16x4(t), pb, acc[2 * kk + ss],
+                                                                                 0, 0, 0);
                 }
             }
         }
