@@ -216,3 +216,51 @@ def test_full_size_workloads_sampled(cid):
         assert att.status() == 0
         assert np.isfinite(out).all()
         check_against_oracle(c, out, lse, req_ids=_sample(c.lengths), what=f"c{cid} mode={mode}")
+
+
+# --------------------------------------------- score ranges beyond 2^8 --
+
+def _shaped_case(profile, kv_dtype, seed):
+    """Scores that rise, fall or spike across the context, spanning hundreds of
+    log2 units, so the running maximum of the online softmax moves many times
+    (every rescale path of the kernel runs) or only once."""
+    L1 = 1500
+    c = _case([L1, 700, 64], Hq=8, Hkv=1, P=16, seed=seed, kv_dtype="bf16")
+    rng = np.random.default_rng(seed)
+    d = c.D
+    q = torch.ones(c.B, c.Hq, d) * 4.0 + torch.from_numpy(rng.normal(0, 0.1, (c.B, c.Hq, d))).float()
+    kf = c.k_cache.float().clone()
+    for b, Lb in enumerate(c.lengths):
+        j = np.arange(int(Lb))
+        if profile == "rising":
+            a = 3.0 * j / max(1, Lb)
+        elif profile == "falling":
+            a = 3.0 * (1 - j / max(1, Lb))
+        else:                        # flat with sparse large spikes
+            a = np.where(j % 97 == 13, 4.0, -1.0)
+        pages = c.page_table[b, j // c.P]
+        for g in range(c.Hkv):
+            kf[pages, g, j % c.P, :] = torch.from_numpy(a[:, None] + rng.normal(0, 0.05, (len(j), d))).float()
+    q = q.to(torch.bfloat16)
+    if kv_dtype == "bf16":
+        return wl.Case(c.name, c.B, c.Hq, c.Hkv, c.D, c.P, c.lengths, c.page_table, c.num_pages, "bf16", q,
+                       kf.to(torch.bfloat16), c.v_cache, None, None, c.sm_scale)
+    vf = c.v_cache.float()
+    ks = wl._owner_scales(kf, c.lengths, c.page_table, c.P)
+    vs = wl._owner_scales(vf, c.lengths, c.page_table, c.P)
+    kc = wl._quantize_owned(kf, ks, c.lengths, c.page_table, c.P)
+    vc = wl._quantize_owned(vf, vs, c.lengths, c.page_table, c.P)
+    return wl.Case(c.name, c.B, c.Hq, c.Hkv, c.D, c.P, c.lengths, c.page_table, c.num_pages, "fp8", q, kc, vc,
+                   ks, vs, c.sm_scale)
+
+
+@pytest.mark.parametrize("profile", ["rising", "falling", "spikes"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_large_score_ranges(profile, kv):
+    c = _shaped_case(profile, kv, seed=60)
+    ref_o, ref_l = oracle.decode(c)
+    assert np.nanmax(ref_l) > 100, "the case must span a wide score range"
+    for fused in (False, True):
+        for W in (1, 7):
+            out, lse, _ = run(c, W=W, fused=fused)
+            check_against_oracle(c, out, lse, what=f"{profile} {kv} W={W} fused={fused}")
