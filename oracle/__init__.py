@@ -7,7 +7,8 @@ package imports nothing from the product.
 
 ``decode`` is the fp64 definition of one decode-attention step (C, in
 ``oracle.c``); ``plan`` is the integer tile-plan specification the GPU planner
-must reproduce byte for byte; ``brute`` holds an independent NumPy two-pass
+must reproduce byte for byte; ``append_kv`` writes one new token per request
+into a paged cache (``e4m3fn_encode`` is its fp8 rounding); ``brute`` holds an independent NumPy two-pass
 softmax used to pin ``decode`` on tiny inputs. Inputs are plain host arrays
 (numpy, or CPU torch tensors), duck-typed on the attribute names of a decode
 step: B, Hq, Hkv, D, P, num_pages, kv_dtype, q, k_cache, v_cache, k_scale,
@@ -42,6 +43,12 @@ def _load():
         lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
         lib.oracle_e4m3fn_to_f64.restype = ctypes.c_double
         lib.oracle_e4m3fn_to_f64.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3fn_encode.restype = ctypes.c_uint8
+        lib.oracle_e4m3fn_encode.argtypes = [ctypes.c_float]
+        lib.oracle_e4m3fn_encode_array.restype = None
+        lib.oracle_e4m3fn_encode_array.argtypes = [P, P, ctypes.c_int64]
+        lib.oracle_append.restype = i32
+        lib.oracle_append.argtypes = [i32] * 7 + [P] * 8
         _lib = lib
     return _lib
 
@@ -72,6 +79,38 @@ def bf16_to_f64(bits: int) -> float:
 
 def e4m3fn_to_f64(code: int) -> float:
     return _load().oracle_e4m3fn_to_f64(int(code) & 0xFF)
+
+
+def e4m3fn_encode(values) -> np.ndarray:
+    """e4m3fn codes (uint8) of fp32 values: nearest, ties to even, saturating."""
+    y = np.ascontiguousarray(values, np.float32)
+    out = np.empty(y.shape, np.uint8)
+    _load().oracle_e4m3fn_encode_array(_ptr(y), _ptr(out), y.size)
+    return out
+
+
+def append_kv(case, k_new, v_new, positions, k_cache=None, v_cache=None, page_table=None, k_scale=None,
+              v_scale=None):
+    """Append one token per request into copies of the caches (see oracle.c).
+    Returns (k_cache, v_cache, status) as host arrays (uint16 bits for bf16,
+    uint8 codes for fp8)."""
+    lib = _load()
+    fp8 = case.kv_dtype == "fp8"
+    kdt = np.uint8 if fp8 else np.uint16
+    kc = np.array(_np(case.k_cache if k_cache is None else k_cache, kdt), copy=True)
+    vc = np.array(_np(case.v_cache if v_cache is None else v_cache, kdt), copy=True)
+    pt = _np(case.page_table if page_table is None else page_table, np.int32)
+    kn = _np(k_new, np.uint16)
+    vn = _np(v_new, np.uint16)
+    pos = _np(positions, np.int32)
+    ks = vs = None
+    if fp8:
+        ks = _np(case.k_scale if k_scale is None else k_scale, np.float32)
+        vs = _np(case.v_scale if v_scale is None else v_scale, np.float32)
+    st = lib.oracle_append(int(case.B), int(case.Hkv), int(case.D), int(case.P), int(case.num_pages),
+                           int(pt.shape[1]), int(fp8), _ptr(kn), _ptr(vn), _ptr(pos), _ptr(pt), _ptr(ks),
+                           _ptr(vs), _ptr(kc), _ptr(vc))
+    return kc, vc, int(st)
 
 
 def decode(case, req_ids=None, threads=0, *, lengths=None, page_table=None, sm_scale=None,

@@ -339,3 +339,94 @@ int oracle_plan(int32_t mode, int32_t B, int32_t Hkv, int32_t P, int32_t pt_stri
     memcpy(header, h, sizeof h);
     return 0;
 }
+
+/* ------------------------------------------------------- KV append -- */
+
+/*
+ * The e4m3fn code nearest to the fp32 value y: ties to even, magnitudes at or
+ * above 448 (the largest finite e4m3fn value) saturate to +-448, NaN gives the
+ * NaN code 0x7F. Written from the format's definition (see
+ * oracle_e4m3fn_to_f64): normal numbers are (8 + m) * 2^(E-3) with E in
+ * [-6, 8] and exponent field E + 7; below 2^-6 the values are the multiples
+ * of 2^-9 with exponent field 0.
+ */
+uint8_t oracle_e4m3fn_encode(float y)
+{
+    if (y != y)
+        return 0x7F;
+    const uint8_t sign = signbit(y) ? 0x80 : 0x00;
+    const double a = fabs((double)y);
+    if (a >= 448.0)
+        return sign | 0x7E;
+    if (a < ldexp(1.0, -6)) {
+        const double m = nearbyint(a * 512.0);   /* exact scaling; 8 is the smallest normal */
+        return sign | (uint8_t)m;
+    }
+    int e;
+    frexp(a, &e);                                /* a = f * 2^e, f in [0.5, 1) */
+    int E = e - 1;
+    double m = nearbyint(ldexp(a, 3 - E));       /* in [8, 16] */
+    if (m == 16.0) {
+        m = 8.0;
+        ++E;
+    }
+    if (E > 8)
+        return sign | 0x7E;
+    return sign | (uint8_t)(((E + 7) << 3) | ((int)m - 8));
+}
+
+void oracle_e4m3fn_encode_array(const float *y, uint8_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_e4m3fn_encode(y[i]);
+}
+
+/*
+ * Append one token per request to a paged cache: request b's new key and value
+ * rows k_new[b][g][:], v_new[b][g][:] (bf16 bits, [B][Hkv][D]) go to token
+ * position positions[b], i.e. row positions[b] % P of page
+ * page_table[b][positions[b] / P]. A bf16 cache stores the bits unchanged; an
+ * fp8 cache stores oracle_e4m3fn_encode(x / scale) with x the bf16 value and
+ * scale = k_scale[b][g] (v_scale for values), the division done in fp32.
+ * A negative position means "no append". A position at or beyond
+ * pt_stride * P sets status bit 1 and a page id outside [0, num_pages) sets
+ * bit 2; such requests are skipped. Returns the status bits.
+ */
+int oracle_append(int32_t B, int32_t Hkv, int32_t D, int32_t P, int32_t num_pages, int32_t pt_stride,
+                  int32_t kv_fp8, const uint16_t *k_new, const uint16_t *v_new, const int32_t *positions,
+                  const int32_t *page_table, const float *k_scale, const float *v_scale, void *k_cache,
+                  void *v_cache)
+{
+    int status = 0;
+    for (int32_t b = 0; b < B; ++b) {
+        const int64_t pos = positions[b];
+        if (pos < 0)
+            continue;
+        if (pos >= (int64_t)pt_stride * P) {
+            status |= 1;
+            continue;
+        }
+        const int64_t page = page_table[(int64_t)b * pt_stride + pos / P];
+        if (page < 0 || page >= num_pages) {
+            status |= 2;
+            continue;
+        }
+        for (int32_t g = 0; g < Hkv; ++g) {
+            const int64_t src = ((int64_t)b * Hkv + g) * D;
+            const int64_t dst = ((page * Hkv + g) * P + pos % P) * D;
+            for (int32_t d = 0; d < D; ++d) {
+                if (kv_fp8) {
+                    const float ks = k_scale[(int64_t)b * Hkv + g], vs = v_scale[(int64_t)b * Hkv + g];
+                    const float kx = (float)oracle_bf16_to_f64(k_new[src + d]);
+                    const float vx = (float)oracle_bf16_to_f64(v_new[src + d]);
+                    ((uint8_t *)k_cache)[dst + d] = oracle_e4m3fn_encode(kx / ks);
+                    ((uint8_t *)v_cache)[dst + d] = oracle_e4m3fn_encode(vx / vs);
+                } else {
+                    ((uint16_t *)k_cache)[dst + d] = k_new[src + d];
+                    ((uint16_t *)v_cache)[dst + d] = v_new[src + d];
+                }
+            }
+        }
+    }
+    return status;
+}

@@ -285,3 +285,83 @@ def test_pins_catch_a_dropped_last_row(tmp_path):
         assert not np.allclose(o, bo, rtol=1e-6, atol=1e-6)
     finally:
         oracle._lib = good_lib
+
+
+# ------------------------------------------------------------ KV append --
+
+def _torch_e4m3fn(y):
+    """Library reference: torch's own float -> float8_e4m3fn conversion, after
+    saturating to the format's largest finite value."""
+    t = torch.from_numpy(np.ascontiguousarray(y, np.float32))
+    return t.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_e4m3fn_encoder_round_trips_every_finite_code():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    vals = np.array([oracle.e4m3fn_to_f64(int(c)) for c in codes], np.float32)
+    assert np.array_equal(oracle.e4m3fn_encode(vals), codes)
+
+
+def test_e4m3fn_encoder_matches_library_on_ties_and_a_dense_sweep():
+    finite = np.array(sorted({oracle.e4m3fn_to_f64(c) for c in range(0x7F)}))   # non-negative values
+    mids = (finite[:-1] + finite[1:]) / 2                                      # exact ties
+    f32 = mids.astype(np.float32)
+    near = np.concatenate([f32, np.nextafter(f32, np.float32(np.inf)), np.nextafter(f32, np.float32(-np.inf))])
+    rng = np.random.default_rng(0)
+    dense = np.concatenate([
+        rng.uniform(0, 2.0 ** -6, 20000), rng.uniform(0, 1, 20000), rng.uniform(0, 500, 20000),
+        np.exp(rng.uniform(np.log(1e-6), np.log(1e6), 20000)), finite, [0.0, 448.0, 449.0, 464.0, 480.0, 1e30],
+    ]).astype(np.float32)
+    y = np.concatenate([near, dense])
+    y = np.concatenate([y, -y])
+    assert np.array_equal(oracle.e4m3fn_encode(y), _torch_e4m3fn(y))
+    assert oracle.e4m3fn_encode(np.array([np.nan], np.float32))[0] == 0x7F
+
+
+def _append_expected(c, k_new, v_new, positions):
+    """Independent construction of the appended caches with torch indexing and
+    torch's conversions (no loop shared with the C reference)."""
+    kc, vc = c.k_cache.clone(), c.v_cache.clone()
+    for b, pos in enumerate(positions):
+        if pos < 0 or pos >= c.pt_stride * c.P:
+            continue
+        page = int(c.page_table[b, pos // c.P])
+        if page < 0 or page >= c.num_pages:
+            continue
+        if c.kv_dtype == "fp8":
+            kq = torch.from_numpy(_torch_e4m3fn((k_new[b].float() / c.k_scale[b][:, None]).numpy()))
+            vq = torch.from_numpy(_torch_e4m3fn((v_new[b].float() / c.v_scale[b][:, None]).numpy()))
+            kc[page, :, pos % c.P] = kq
+            vc[page, :, pos % c.P] = vq
+        else:
+            kc[page, :, pos % c.P] = k_new[b]
+            vc[page, :, pos % c.P] = v_new[b]
+    return kc, vc
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_append_reference_against_independent_construction(kv):
+    c = _case([5, 16, 31, 0], Hq=4, Hkv=2, P=16, kv_dtype=kv, seed=21, pt_stride=3, extra_pages=2)
+    rng = np.random.default_rng(3)
+    k_new = torch.from_numpy(rng.normal(0, 3, (c.B, c.Hkv, c.D)).astype(np.float32)).to(torch.bfloat16)
+    v_new = torch.from_numpy(rng.normal(0, 3, (c.B, c.Hkv, c.D)).astype(np.float32)).to(torch.bfloat16)
+    pos = np.array([5, 16, 31, 0], np.int32)             # new pages at 16 (page 1) need a page id
+    pt = c.page_table.copy()
+    pt[1, 1] = c.num_pages - 1
+    pt[3, 0] = c.num_pages - 2
+    c2 = wl.Case(c.name, c.B, c.Hq, c.Hkv, c.D, c.P, c.lengths, pt, c.num_pages, c.kv_dtype, c.q, c.k_cache,
+                 c.v_cache, c.k_scale, c.v_scale, c.sm_scale)
+    kc, vc, st = oracle.append_kv(c2, k_new, v_new, pos)
+    ek, ev = _append_expected(c2, k_new, v_new, pos)
+    view = torch.uint8 if kv == "fp8" else torch.int16
+    assert st == 0
+    assert np.array_equal(kc.view(ek.view(view).numpy().dtype), ek.view(view).numpy())
+    assert np.array_equal(vc.view(ev.view(view).numpy().dtype), ev.view(view).numpy())
+    # skips: no append (-1), a position past the page table (bit 1), a bad page id (bit 2)
+    pt[2, 1] = c.num_pages + 7
+    c3 = wl.Case(c.name, c.B, c.Hq, c.Hkv, c.D, c.P, c.lengths, pt, c.num_pages, c.kv_dtype, c.q, c.k_cache,
+                 c.v_cache, c.k_scale, c.v_scale, c.sm_scale)
+    kc, vc, st = oracle.append_kv(c3, k_new, v_new, np.array([-1, 48, 17, 0], np.int32))
+    assert st == 3
+    ek, ev = _append_expected(c3, k_new, v_new, [-1, -1, -1, 0])
+    assert np.array_equal(kc.view(ek.view(view).numpy().dtype), ek.view(view).numpy())
