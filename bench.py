@@ -252,19 +252,36 @@ def batch_leg(cid, torch, L, wl, W_of, flush, static_sweep=False):
 def trace_leg(torch, L, W_of, flush, steps=256):
     """Workload 4: the continuous-batching trace with an fp8 cache. Each step is
     timed alone after a cache flush: the single-launch step (its plan is built
-    inside the kernel) and the three-launch step (attn_plan included). Host
-    updates and uploads happen between steps, outside the timed region."""
+    inside the kernel) and the three-launch step (attn_plan included). Between
+    steps the host draws the new tokens and requests and uploads the small
+    arrays; each step's appended K/V rows are written on the device by
+    attn_append_kv, timed on its own and also reported added to the step."""
     from variable_length_kv_amd import workloads as wl
     from variable_length_kv_amd.trace import DeviceTrace
     t0 = time.perf_counter()
     tr = wl.Trace(steps=steps)
-    dt = DeviceTrace(tr)
-    log(f"bench: trace generated in {time.perf_counter() - t0:.1f} s ({tr.num_pages} pages)")
     W = W_of(tr.lengths, tr.Hkv)
     shape = L.AttnShape(batch=tr.slots, num_q_heads=tr.Hq, num_kv_heads=tr.Hkv, page_size=tr.P,
                         num_pages=tr.num_pages, pt_stride=tr.pt_stride, num_wgs=W,
                         kv_dtype=L.ATTN_KV_FP8_E4M3)
     att = L.Attention(shape, "cuda:0")
+    append_ev, append_host = [], []
+
+    def timed_append(*args):
+        # The step's new rows written on the device (attn_append_kv), timed
+        # alone: queued behind the cache sweep so that the events see the kernel
+        # and not the host's time to issue it (which is recorded apart).
+        flush.sum()
+        e0, e1 = ev(torch), ev(torch)
+        e0.record()
+        h0 = time.perf_counter()
+        att.append_kv(*args)
+        append_host.append(time.perf_counter() - h0)
+        e1.record()
+        append_ev.append((e0, e1))
+
+    dt = DeviceTrace(tr, append=timed_append)
+    log(f"bench: trace generated in {time.perf_counter() - t0:.1f} s ({tr.num_pages} pages)")
     out = torch.empty_like(dt.q)
     lse = torch.empty(tr.slots, tr.Hq, dtype=torch.float32, device="cuda:0")
     sm = 1.0 / math.sqrt(tr.D)
@@ -303,6 +320,8 @@ def trace_leg(torch, L, W_of, flush, steps=256):
         if dt.step == steps - 1:
             break
         dt.advance()
+    torch.cuda.synchronize()
+    ta = np.array([a.elapsed_time(b) for a, b in append_ev]) * 1e3   # us, steps 1..
     tf = np.array(tf) * 1e3   # us
     t3 = np.array(t3) * 1e3
     t3s = t3.sum(axis=1)
@@ -320,6 +339,11 @@ def trace_leg(torch, L, W_of, flush, steps=256):
     out_d = {"steps": steps, "num_wgs": W, "kv_gb_mean": round(float(kvb.mean()) / 1e9, 4),
              "single_launch": summary(tf),
              "three_launch": summary(t3s)}
+    with_append = tf[1:] + ta
+    out_d["append_us_median"] = round(float(np.median(ta)), 2)
+    out_d["append_host_issue_us_median"] = round(float(np.median(append_host)) * 1e6, 2)
+    out_d["single_launch_with_append"] = {"us_per_step_median": round(float(np.median(with_append)), 2),
+                                          "us_per_step_p99": round(float(np.percentile(with_append, 99)), 2)}
     out_d["three_launch"].update({"plan_us_median": round(float(np.median(t3[:, 0])), 2),
                                   "decode_us_median": round(float(np.median(t3[:, 1])), 2),
                                   "combine_us_median": round(float(np.median(t3[:, 2])), 2)})

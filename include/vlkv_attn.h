@@ -197,6 +197,34 @@ int attn_step(const attn_shape *shape, const void *q, const void *k_cache, const
               void *out, float *lse, void *stream);
 
 /*
+ * Append one new token per request to the paged caches: the step that grows
+ * every context by one token before decode attends to it (contexts that grow
+ * at different rates under continuous batching, [Tencent HPC lands in SGLang,
+ * challenging default inference kernels, sec. "Why Tencent HPC matters for
+ * online model serving"]; cache precision, sec. "What the 48.8% TPOT claim does
+ * not prove").
+ *   k_new, v_new (device) bf16 [B][Hkv][D]: the new key and value rows
+ *   positions    (device) int32 [B]: token position to write (normally the
+ *                length before the append); a negative value skips the request
+ *   page_table   (device) int32 [B][pt_stride]; the page of the position must
+ *                already be assigned
+ *   k_scale, v_scale (device) fp32 [B][Hkv] for ATTN_KV_FP8_E4M3, else NULL
+ *   k_cache, v_cache (device) [num_pages][Hkv][P][D], written in place: row
+ *                positions[b] % P of page page_table[b][positions[b] / P]
+ *   workspace    (device, optional) a workspace of this shape whose status word
+ *                receives ATTN_STATUS_BAD_LENGTH for a position at or beyond
+ *                pt_stride * P and ATTN_STATUS_BAD_PAGE for a page id outside
+ *                [0, num_pages); such requests are skipped. NULL: no status.
+ * bf16 caches store the bits of the new rows. fp8 caches store the OCP e4m3fn
+ * code of x / scale (fp32 division, nearest with ties to even, saturated at
+ * +-448). Only the rows written are touched.
+ */
+int attn_append_kv(const attn_shape *shape, const void *k_new, const void *v_new,
+                   const int32_t *positions, const int32_t *page_table, const float *k_scale,
+                   const float *v_scale, void *k_cache, void *v_cache, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
+/*
  * Copy the status word of the last plan/decode on this workspace into *flags
  * (host pointer). SYNCHRONISES `stream`; meant for tests and debugging, not
  * for the per-step path.

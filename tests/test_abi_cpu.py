@@ -109,3 +109,17 @@ def test_suggested_workgroup_count():
     assert L.suggest_num_wgs(4, [0, -5], 1) == 4
     assert L.suggest_num_wgs(2, [64 * 32 * 4], 1) == 4                 # exactly 32 tiles per workgroup
     assert L.suggest_num_wgs(2, [64 * 32 * 4 - 64], 1) == 2
+
+
+def test_append_rejects_bad_arguments_before_launch():
+    lib = L.load()
+    s = _shape().c()
+    nz = ctypes.c_void_p(256)       # a non-null, 16-byte aligned stand-in; never dereferenced on error paths
+    args = [nz, nz, nz, nz, None, None, nz, nz, None, 0, None]
+    assert lib.attn_append_kv(ctypes.byref(s), None, *args[1:]) == L.ATTN_ERR_INVALID_ARG
+    assert b"non-NULL" in lib.attn_last_error()
+    fp8 = _shape(kv_dtype=L.ATTN_KV_FP8_E4M3).c()
+    assert lib.attn_append_kv(ctypes.byref(fp8), *args) == L.ATTN_ERR_INVALID_ARG   # scales missing
+    odd = ctypes.c_void_p(258)
+    assert lib.attn_append_kv(ctypes.byref(s), odd, *args[1:]) == L.ATTN_ERR_INVALID_ARG
+    assert b"aligned" in lib.attn_last_error()

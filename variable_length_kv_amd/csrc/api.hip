@@ -398,6 +398,50 @@ int attn_step(const attn_shape *shape, const void *q, const void *k_cache, const
     return ok();
 }
 
+int attn_append_kv(const attn_shape *shape, const void *k_new, const void *v_new, const int32_t *positions,
+                   const int32_t *page_table, const float *k_scale, const float *v_scale, void *k_cache,
+                   void *v_cache, void *workspace, size_t workspace_bytes, void *stream)
+{
+    Shape s;
+    WsLayout L;
+    int rc = check(shape, &s);
+    if (rc != ATTN_OK)
+        return rc;
+    if (!k_new || !v_new || !positions || !page_table || !k_cache || !v_cache)
+        return fail(ATTN_ERR_INVALID_ARG,
+                    "k_new, v_new, positions, page_table, k_cache and v_cache must be non-NULL");
+    if (s.kv_fp8 && (!k_scale || !v_scale))
+        return fail(ATTN_ERR_INVALID_ARG, "fp8 cache needs k_scale and v_scale");
+    if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new) |
+         reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache)) % 16)
+        return fail(ATTN_ERR_INVALID_ARG, "new rows and caches must be 16-byte aligned");
+    int32_t *header = nullptr;
+    if (workspace) {
+        if ((rc = check_ws(s, workspace, workspace_bytes, &L)) != ATTN_OK)
+            return rc;
+        header = at<int32_t>(workspace, L.header);
+    }
+    AppendArgs a;
+    a.k_new = static_cast<const uint16_t *>(k_new);
+    a.v_new = static_cast<const uint16_t *>(v_new);
+    a.positions = positions;
+    a.page_table = page_table;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.k_cache = static_cast<uint8_t *>(k_cache);
+    a.v_cache = static_cast<uint8_t *>(v_cache);
+    a.header = header;
+    a.B = s.B;
+    a.Hkv = s.Hkv;
+    a.P = s.P;
+    a.num_pages = s.num_pages;
+    a.pt_stride = s.pt_stride;
+    const hipError_t e = launch_append(a, s.kv_fp8, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "append launch");
+    return ok();
+}
+
 int attn_get_status(const void *workspace, uint32_t *flags, void *stream)
 {
     if (!workspace || !flags)

@@ -73,7 +73,18 @@ struct CombineArgs {
     int B, Hq, Hkv, G, mode, S;
 };
 
+struct AppendArgs {
+    const uint16_t *k_new, *v_new;   // [B][Hkv][D] bf16 bits
+    const int32_t *positions;        // [B]
+    const int32_t *page_table;       // [B][pt_stride]
+    const float *k_scale, *v_scale;  // [B][Hkv] (fp8 only)
+    uint8_t *k_cache, *v_cache;      // [num_pages][Hkv][P][D]
+    int32_t *header;                 // status word, or null
+    int B, Hkv, P, num_pages, pt_stride;
+};
+
 hipError_t launch_plan(const PlanArgs &a, hipStream_t st);
+hipError_t launch_append(const AppendArgs &a, int kv_fp8, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs &a, int src, int kv_fp8, int grid, hipStream_t st);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t st);
 hipError_t launch_ws_init(int32_t *header, int32_t *counters, int n_counters, hipStream_t st);

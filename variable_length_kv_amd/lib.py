@@ -24,7 +24,7 @@ ATTN_STATUS_BAD_LENGTH, ATTN_STATUS_BAD_PAGE = 1, 2
 
 EXPORTED = ("attn_check_shape", "attn_workspace_bytes", "attn_static_splits", "attn_device_cu_count",
             "attn_plan", "attn_decode", "attn_combine", "attn_get_status", "attn_read_plan",
-            "attn_workspace_init", "attn_step", "attn_last_error")
+            "attn_workspace_init", "attn_step", "attn_append_kv", "attn_last_error")
 
 
 class AttnError(RuntimeError):
@@ -85,6 +85,7 @@ def load():
         "attn_read_plan": (i32, [SP, P, P, P, P, P, P, P, P, P]),
         "attn_workspace_init": (i32, [SP, P, sz, P]),
         "attn_step": (i32, [SP, P, P, P, P, P, P, P, ctypes.c_float, P, sz, P, P, P]),
+        "attn_append_kv": (i32, [SP, P, P, P, P, P, P, P, P, P, sz, P]),
         "attn_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sigs.items():
@@ -119,8 +120,9 @@ def _stream(stream):
 
 
 def _shape(shape):
-    s = shape.c() if isinstance(shape, AttnShape) else shape
-    return ctypes.byref(s)
+    if isinstance(shape, AttnShape):
+        shape = shape.c()
+    return ctypes.byref(shape)
 
 
 def attn_check_shape(shape) -> None:
@@ -185,6 +187,14 @@ def attn_step(shape, q, k_cache, v_cache, k_scale, v_scale, page_table, lengths,
                             workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(stream)))
 
 
+def attn_append_kv(shape, k_new, v_new, positions, page_table, k_cache, v_cache, k_scale=None, v_scale=None,
+                   workspace=None, stream=None) -> None:
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().attn_append_kv(_shape(shape), _ptr(k_new), _ptr(v_new), _ptr(positions), _ptr(page_table),
+                                 _ptr(k_scale), _ptr(v_scale), _ptr(k_cache), _ptr(v_cache), _ptr(workspace),
+                                 nbytes, _stream(stream)))
+
+
 def attn_get_status(workspace, stream=None) -> int:
     out = ctypes.c_uint32()
     _check(load().attn_get_status(_ptr(workspace), ctypes.byref(out), _stream(stream)))
@@ -222,11 +232,16 @@ class Attention:
         off = (-self.workspace.data_ptr()) % 256
         self.workspace = self.workspace[off:off + n]
         attn_workspace_init(shape, self.workspace, stream)
+        # per-call arguments that do not change (the shape is not to be edited
+        # after construction): the C shape and the workspace
+        self._cshape = ctypes.byref(shape.c())
+        self._ws = (ctypes.c_void_p(self.workspace.data_ptr()), n)
 
     def fused_step(self, q, k_cache, v_cache, page_table, lengths, sm_scale, out, lse=None, k_scale=None,
                    v_scale=None, stream=None):
-        attn_step(self.shape, q, k_cache, v_cache, k_scale, v_scale, page_table, lengths, sm_scale,
-                  self.workspace, out, lse, stream)
+        _check(load().attn_step(self._cshape, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                _ptr(v_scale), _ptr(page_table), _ptr(lengths), float(sm_scale), self._ws[0],
+                                self._ws[1], _ptr(out), _ptr(lse), _stream(stream)))
 
     def plan(self, lengths, page_table, stream=None):
         attn_plan(self.shape, lengths, page_table, self.workspace, stream)
@@ -244,6 +259,12 @@ class Attention:
         self.plan(lengths, page_table, stream)
         self.decode(q, k_cache, v_cache, page_table, sm_scale, out, lse, k_scale, v_scale, stream)
         self.combine(out, lse, stream)
+
+    def append_kv(self, k_new, v_new, positions, page_table, k_cache, v_cache, k_scale=None, v_scale=None,
+                  stream=None):
+        _check(load().attn_append_kv(self._cshape, _ptr(k_new), _ptr(v_new), _ptr(positions), _ptr(page_table),
+                                     _ptr(k_scale), _ptr(v_scale), _ptr(k_cache), _ptr(v_cache), self._ws[0],
+                                     self._ws[1], _stream(stream)))
 
     def status(self, stream=None) -> int:
         return attn_get_status(self.workspace, stream)

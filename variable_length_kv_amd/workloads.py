@@ -355,7 +355,8 @@ class Trace:
     def advance(self):
         """Apply the transition step -> step+1. Returns a dict of patches:
         rows: (pages, slots_in_page) int64 tensors of appended token rows;
-        pages: int64 tensor of pages rewritten whole; slots: slots whose scales changed."""
+        pages: int64 tensor of pages rewritten whole; slots: slots whose scales changed
+        (replaced requests); new_k, new_v: the appended bf16 rows [slots, Hkv, D]."""
         s = self.step
         if s >= self.steps - 1:
             raise StopIteration
@@ -403,4 +404,5 @@ class Trace:
             "rows": (torch.tensor(row_pages, dtype=torch.int64), torch.tensor(row_slots, dtype=torch.int64)),
             "pages": torch.tensor(sorted(set(new_pages)), dtype=torch.int64),
             "slots": [slot for slot, _ in self.events[s]],
+            "new_k": kn, "new_v": vn,
         }
