@@ -53,6 +53,7 @@ typedef short s16x4 __attribute__((__vector_size__(4 * sizeof(short))));
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kLdsRow = kHeadDim + 4;  // padded fp32 row of the merge buffer
 constexpr float kLazy = 8.f;           // lazy-rescale threshold (log2 units)
+constexpr int kMergeBatch = 4;         // partials folded together by the LSE merge
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -167,12 +168,23 @@ struct Walker {
     __device__ int64_t owner(int64_t u) const { return div_floor((u + 1) * We - 1, N); }
     __device__ int64_t begin_of(int64_t ww) const { return div_floor(ww * N, We); }
 
+    // single launch, dynamic: the prologue's LDS copies of the tiles prefix and
+    // the validated lengths, used until the block loop starts (then nullptr)
+    const int32_t *ltp = nullptr, *llen = nullptr;
+
     __device__ int tiles_of(int bb) const
     {
+        if (kFused && ltp)
+            return __builtin_amdgcn_readfirstlane(ltp[bb + 1]) - __builtin_amdgcn_readfirstlane(ltp[bb]);
         return kFused ? (len_valid(a, bb) + a->T - 1) / a->T
                       : ldc(a->tiles_prefix, bb + 1) - ldc(a->tiles_prefix, bb);
     }
-    __device__ int length_of(int bb) const { return kFused ? len_valid(a, bb) : ldc(a->len_eff, bb); }
+    __device__ int length_of(int bb) const
+    {
+        if (kFused && llen)
+            return __builtin_amdgcn_readfirstlane(llen[bb]);
+        return kFused ? len_valid(a, bb) : ldc(a->len_eff, bb);
+    }
 
     __device__ void enter_segment(int ta, int tb)
     {
@@ -202,11 +214,15 @@ struct Walker {
         }
     }
 
-    // lds_tp: tiles prefix (single launch, dynamic only)
-    __device__ void init(const DecodeArgs *args, int wg, int wv, const int32_t *lds_tp, int64_t N_, int64_t We_,
-                         int chunk)
+    // lds_tp, lds_len: tiles prefix and validated lengths (single launch, dynamic only)
+    __device__ void init(const DecodeArgs *args, int wg, int wv, const int32_t *lds_tp, const int32_t *lds_len,
+                         int64_t N_, int64_t We_, int chunk)
     {
         a = args;
+        if (SRC == SRC_FUSED_DYNAMIC) {
+            ltp = lds_tp;
+            llen = lds_len;
+        }
         w = wg;
         wave = wv;
         done = 0;
@@ -364,28 +380,73 @@ __device__ __forceinline__ float load_coherent(const float *p)
     return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Merge n partial results (o normalised, lse in base 2) of one (request, kv
-// head) pair into the bf16 output and the natural-log lse. slot_of(s) gives the
-// slot of the s-th partial. Run by all threads of a workgroup. COHERENT reads
-// the partials with agent-scope loads (partials written in the same launch).
+// The LSE merge of partial results (o normalised, lse in base 2) of one
+// (request, kv head) pair, for one (head, 4 dims) of the output. The running
+// state is M (largest lse so far), den = sum 2^(lse_s - M) and
+// o = sum 2^(lse_s - M) o_s; partials are folded in slot order, kMergeBatch at a
+// time. Both merges (the combine kernel and the single launch's last arriver)
+// go through these two functions, with contraction off, so they round
+// identically wherever they are inlined.
+__device__ __forceinline__ void merge_fold(float &M, float &den, f32x4 &o, const float (&ls)[kMergeBatch],
+                                           const f32x4 (&xs)[kMergeBatch], int nb)
+{
+#pragma clang fp contract(off)
+    float Mb = M;
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j)
+        if (j < nb)
+            Mb = fmaxf(Mb, ls[j]);
+    if (Mb == -INFINITY)
+        return;   // every partial so far is empty
+    const float r = fast_exp2(M - Mb);   // 0 when M is -inf
+    den *= r;
+    o *= r;
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+        if (j < nb) {
+            const float e = fast_exp2(ls[j] - Mb);
+            den += e;
+            o += e * xs[j];
+        }
+    }
+    M = Mb;
+}
+
+// Final step of the merge: o / den as bf16 and the natural-log lse.
+__device__ __forceinline__ void merge_write(float M, float den, f32x4 o, uint16_t *out, float *lse, size_t hq, int d4)
+{
+#pragma clang fp contract(off)
+    float lse2 = -INFINITY;
+    if (M != -INFINITY) {
+        o *= 1.f / den;
+        lse2 = M + log2f(den);
+    } else {
+        o = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    *reinterpret_cast<bf16x4 *>(out + hq * kHeadDim + d4) = __builtin_convertvector(o, bf16x4);
+    if (lse && d4 == 0)
+        lse[hq] = lse2 * kLn2;
+}
+
+// Merge n partials of one (request, kv head) pair into the bf16 output and the
+// natural-log lse. slot_of(s) gives the slot of the s-th partial. Run by all
+// threads of a workgroup. COHERENT reads the partials with agent-scope loads
+// (partials written in the same launch).
 template <bool COHERENT, typename SlotOf>
 __device__ __forceinline__ void merge_partials(const float *part_o, const float *part_lse, int n, SlotOf slot_of,
                                                int G, int Hq, int b, int g, uint16_t *out, float *lse)
 {
     constexpr int D = kHeadDim;
-    constexpr int kBatch = 4;   // partials whose loads are issued together
     auto ld = [](const float *p) { return COHERENT ? load_coherent(p) : *p; };
     for (int idx = threadIdx.x; idx < G * 32; idx += kDecodeThreads) {
         const int h = idx >> 5, d4 = (idx & 31) * 4;
-        // running merge: M the largest lse so far, den = sum 2^(lse_s - M),
-        // o = sum 2^(lse_s - M) o_s
         float M = -INFINITY, den = 0.f;
         f32x4 o = {0.f, 0.f, 0.f, 0.f};
-        for (int s0 = 0; s0 < n; s0 += kBatch) {
-            float ls[kBatch];
-            f32x4 xs[kBatch];
+        for (int s0 = 0; s0 < n; s0 += kMergeBatch) {
+            float ls[kMergeBatch];
+            f32x4 xs[kMergeBatch];
 #pragma unroll
-            for (int j = 0; j < kBatch; ++j) {
+            for (int j = 0; j < kMergeBatch; ++j) {
                 const size_t sl = (size_t)slot_of(s0 + j < n ? s0 + j : s0) * G + h;
                 ls[j] = ld(part_lse + sl);
                 const float *po = part_o + sl * D + d4;
@@ -394,44 +455,19 @@ __device__ __forceinline__ void merge_partials(const float *part_o, const float 
                 else
                     xs[j] = *reinterpret_cast<const f32x4 *>(po);
             }
-            float Mb = M;
-#pragma unroll
-            for (int j = 0; j < kBatch; ++j)
-                if (s0 + j < n)
-                    Mb = fmaxf(Mb, ls[j]);
-            if (Mb == -INFINITY)
-                continue;   // every partial so far is empty
-            const float r = fast_exp2(M - Mb);   // 0 when M is -inf
-            den *= r;
-            o *= r;
-#pragma unroll
-            for (int j = 0; j < kBatch; ++j) {
-                if (s0 + j < n) {
-                    const float e = fast_exp2(ls[j] - Mb);
-                    den += e;
-                    o += e * xs[j];
-                }
-            }
-            M = Mb;
+            merge_fold(M, den, o, ls, xs, n - s0);
         }
-        float lse2 = -INFINITY;
-        if (M != -INFINITY) {
-            o *= 1.f / den;
-            lse2 = M + log2f(den);
-        } else {
-            o = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        const size_t hq = (size_t)b * Hq + (size_t)g * G + h;
-        *reinterpret_cast<bf16x4 *>(out + hq * D + d4) = __builtin_convertvector(o, bf16x4);
-        if (lse && d4 == 0)
-            lse[hq] = lse2 * kLn2;
+        merge_write(M, den, o, out, lse, (size_t)b * Hq + (size_t)g * G + h, d4);
     }
 }
 
 struct DecodeLds {
     union {
         float acc[kWaves][kMaxGroup][kLdsRow];  // per-wave states at a segment's end
-        int32_t tp[kMaxBatch + 1];              // single launch: tiles prefix (prologue only)
+        struct {
+            int32_t tp[kMaxBatch + 1];          // single launch: tiles prefix (prologue only)
+            int32_t len[kMaxBatch];             // and validated lengths
+        };
     };
     float m[kWaves][kMaxGroup];
     float l[kWaves][kMaxGroup];
@@ -475,8 +511,10 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
             bad |= Lb != raw;
             mx = max(mx, Lb);
             const int n = (Lb + a.T - 1) / a.T;
-            if (SRC == SRC_FUSED_DYNAMIC)
+            if (SRC == SRC_FUSED_DYNAMIC) {
                 lds.tp[bb + 1] = n;
+                lds.len[bb] = Lb;
+            }
             sum += n;
         }
         int maxle, bits;
@@ -495,9 +533,12 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
             }
             if (tid == 0)
                 lds.tp[0] = 0;
+            N = (int64_t)total * a.Hkv;
+            We = N < a.W ? N : a.W;
+            __syncthreads();   // the tiles prefix and the lengths are complete
             // requests without tiles: o = 0, lse = -inf (spread over the grid)
             for (int bb = w; bb < a.B; bb += gridDim.x) {
-                if (len_valid(&a, bb) != 0)
+                if (lds.len[bb] != 0)
                     continue;
                 for (int idx = tid; idx < a.Hq * 32; idx += kDecodeThreads) {
                     const int h = idx >> 5, d4 = (idx & 31) * 4;
@@ -507,9 +548,6 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
                         a.lse[hq] = -INFINITY;
                 }
             }
-            N = (int64_t)total * a.Hkv;
-            We = N < a.W ? N : a.W;
-            __syncthreads();   // the tiles prefix is complete
             if (w >= We)
                 return;
         } else {
@@ -539,9 +577,12 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
     }
 
     Walker<SRC> wk;
-    wk.init(&a, w, wave, lds.tp, N, We, chunk);
-    if (SRC == SRC_FUSED_DYNAMIC)
-        __syncthreads();   // every wave has read the tiles prefix; lds.acc may now be written
+    wk.init(&a, w, wave, lds.tp, lds.len, N, We, chunk);
+    const int nblk = wk.count_blocks();
+    if (SRC == SRC_FUSED_DYNAMIC) {
+        wk.ltp = wk.llen = nullptr;   // from here on the walker reads lengths from memory
+        __syncthreads();   // every wave is done with the LDS prefix; lds.acc may now be written
+    }
 
     // per-wave softmax state, head = row. m_run is uniform over the 4 row
     // groups; l_run is this lane's partial sum, reduced at segment end.
@@ -823,7 +864,6 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
     // handled in each iteration; trailing invalid blocks do nothing. (Three or
     // four slots measured slower on gfx950 for both cache types: more registers,
     // no more useful bytes in flight.)
-    const int nblk = wk.count_blocks();
     Slot sl[kSlots];
     Meta mt[kSlots];
 #pragma unroll
