@@ -39,6 +39,8 @@ def _load():
         lib.oracle_decode.argtypes = [i32] * 8 + [P] * 7 + [ctypes.c_double, P, i32, P, P, i32]
         lib.oracle_plan.restype = i32
         lib.oracle_plan.argtypes = [i32] * 8 + [P] * 8
+        lib.oracle_plan_shared.restype = i32
+        lib.oracle_plan_shared.argtypes = [i32] * 8 + [P] * 16
         lib.oracle_bf16_to_f64.restype = ctypes.c_double
         lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
         lib.oracle_e4m3fn_to_f64.restype = ctypes.c_double
@@ -167,4 +169,41 @@ def plan(mode, lengths, Hkv, P, pt_stride, T, W, S=0):
                                                   "first_wg", "wg_begin", "wg_start_b")])
     if rc != 0:
         raise ValueError(f"oracle_plan failed with code {rc}")
+    return out
+
+
+def plan_shared(lengths, page_table, Hkv, G, P, num_pages, T, W):
+    """Integer plan with prefix-shared pages (mode 2). Returns a dict of int32
+    arrays; the item arrays are cut to the number of items."""
+    lib = _load()
+    lengths = _np(lengths, np.int32)
+    pt = np.ascontiguousarray(_np(page_table, np.int32))
+    B = len(lengths)
+    pt_stride = int(pt.shape[1]) if pt.ndim == 2 else 0
+    if pt.ndim != 2 or pt.shape[0] != B:
+        raise ValueError("page_table must be [B][pt_stride]")
+    I2 = max(1, 2 * B)
+    out = {
+        "header": np.zeros(8, np.int32),
+        "item_req": np.zeros(I2, np.int32), "item_start": np.zeros(I2, np.int32),
+        "item_len": np.zeros(I2, np.int32), "item_m": np.zeros(I2, np.int32), "item_solo": np.zeros(I2, np.int32),
+        "req_shared": np.zeros(B, np.int32), "req_member": np.zeros(B, np.int32), "req_own": np.zeros(B, np.int32),
+        "tiles_prefix": np.zeros(I2 + 1, np.int32),
+        "seg_prefix": np.zeros(I2 * Hkv + 1, np.int32),
+        "first_wg": np.zeros(I2 * Hkv, np.int32),
+        "wg_begin": np.zeros(W + 1, np.int32),
+        "wg_start": np.zeros(W, np.int32),
+    }
+    keys = ("header", "item_req", "item_start", "item_len", "item_m", "item_solo", "req_shared", "req_member",
+            "req_own", "tiles_prefix", "seg_prefix", "first_wg", "wg_begin", "wg_start")
+    rc = lib.oracle_plan_shared(B, Hkv, G, P, pt_stride, num_pages, T, W, _ptr(lengths), _ptr(pt),
+                                *[_ptr(out[k]) for k in keys])
+    if rc != 0:
+        raise ValueError(f"oracle_plan_shared failed with code {rc}")
+    I = int(out["header"][4])
+    for k in ("item_req", "item_start", "item_len", "item_m", "item_solo"):
+        out[k] = out[k][:I]
+    out["tiles_prefix"] = out["tiles_prefix"][:I + 1]
+    out["seg_prefix"] = out["seg_prefix"][:I * Hkv + 1]
+    out["first_wg"] = out["first_wg"][:I * Hkv]
     return out

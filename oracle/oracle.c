@@ -342,6 +342,181 @@ int oracle_plan(int32_t mode, int32_t B, int32_t Hkv, int32_t P, int32_t pt_stri
 
 /* ------------------------------------------------------- KV append -- */
 
+/* ---------------------------------------------------- prefix-shared plan -- */
+/*
+ * Integer specification of the plan with prefix-shared pages (mode 2). The
+ * source article lists prefix caching among the situations the kernels must
+ * handle [Tencent HPC lands in SGLang, challenging default inference kernels,
+ * sec. "Why Tencent HPC matters for online model serving", the production-
+ * reliability paragraph]; requests whose page tables begin with the same
+ * physical pages hold the same cached rows there. This plan reads such a
+ * shared prefix once for several requests. The result is the same attention
+ * (the oracle decode above, per request); only the work decomposition changes:
+ *
+ * 1. Le_b = L_b if 0 <= L_b <= pt_stride * P, else 0 (status bit 1).
+ * 2. share_b (b >= 1): c = number of leading page slots j < min(ceil(Le_b / P),
+ *    ceil(Le_{b-1} / P)) with page_table[b][j] == page_table[b-1][j] and that
+ *    id valid (0 <= id < num_pages); share_b = min(c P, Le_b, Le_{b-1}) rounded
+ *    down to a multiple of T. share_0 = 0.
+ * 3. Runs: a run starts at b = 0 and at every b with share_b = 0. A run is cut,
+ *    from its start, into groups of R = max(1, 16 / G) consecutive requests
+ *    (16 query rows per pass: R requests times G query heads of one kv head).
+ *    A group with m >= 2 members shares Ls = min of share over its members
+ *    other than the first (its pages agree with the first member's there).
+ * 4. Items, in request order: a group leader with m >= 2 first emits the
+ *    shared item (req = leader, start 0, len Ls, m members, solo 0); every
+ *    request then emits its own item: (b, Ls, Le_b - Ls, 1, 0) inside a group
+ *    of m >= 2, else (b, 0, Le_b, 1, 1). req_shared[b] / req_member[b] /
+ *    req_own[b] map requests to items (-1 / 0 without a shared item).
+ * 5. From here on mode 0 with items in place of requests: tiles ceil(len/T),
+ *    units (item, kv head, tile) in order, W_eff contiguous ranges, segments
+ *    and their prefix over (item, kv head) pairs, each workgroup's first item.
+ *
+ * header = {status, N, W_eff, max Le, number of items, R, total tiles, T}.
+ * Item arrays hold up to 2B entries; tiles_prefix 2B+1; seg_prefix
+ * 2B*Hkv+1; first_wg 2B*Hkv; wg_begin W+1; wg_start W.
+ */
+int oracle_plan_shared(int32_t B, int32_t Hkv, int32_t G, int32_t P, int32_t pt_stride, int32_t num_pages,
+                       int32_t T, int32_t W, const int32_t *lengths, const int32_t *page_table, int32_t *header,
+                       int32_t *item_req, int32_t *item_start, int32_t *item_len, int32_t *item_m,
+                       int32_t *item_solo, int32_t *req_shared, int32_t *req_member, int32_t *req_own,
+                       int32_t *tiles_prefix, int32_t *seg_prefix, int32_t *first_wg, int32_t *wg_begin,
+                       int32_t *wg_start)
+{
+    if (B < 0 || Hkv <= 0 || G <= 0 || P <= 0 || pt_stride < 0 || num_pages <= 0 || T <= 0 || W <= 0)
+        return ORACLE_EINVAL;
+    const int32_t R = G >= 16 ? 1 : 16 / G;
+    int32_t status = 0;
+    int64_t maxle = 0;
+    int32_t *Le = calloc((size_t)(B > 0 ? B : 1), sizeof *Le);
+    int32_t *share = calloc((size_t)(B > 0 ? B : 1), sizeof *share);
+    if (!Le || !share) {
+        free(Le);
+        free(share);
+        return -5;
+    }
+    /* 1. validated lengths */
+    for (int32_t b = 0; b < B; ++b) {
+        int64_t L = lengths[b];
+        if (L < 0 || L > (int64_t)pt_stride * P) {
+            status |= 1;
+            L = 0;
+        }
+        Le[b] = (int32_t)L;
+        if (L > maxle)
+            maxle = L;
+    }
+    /* 2. tokens shared with the previous request */
+    for (int32_t b = 1; b < B; ++b) {
+        const int64_t na = ((int64_t)Le[b] + P - 1) / P, nb = ((int64_t)Le[b - 1] + P - 1) / P;
+        const int64_t n = na < nb ? na : nb;
+        int64_t c = 0;
+        while (c < n) {
+            const int32_t x = page_table[(int64_t)b * pt_stride + c];
+            const int32_t y = page_table[(int64_t)(b - 1) * pt_stride + c];
+            if (x != y || x < 0 || x >= num_pages)
+                break;
+            ++c;
+        }
+        int64_t t = c * P;
+        if (t > Le[b])
+            t = Le[b];
+        if (t > Le[b - 1])
+            t = Le[b - 1];
+        share[b] = (int32_t)(t / T * T);
+    }
+    /* 3 + 4. groups and items */
+    int64_t I = 0, total = 0;
+    int32_t run0 = 0;
+    tiles_prefix[0] = 0;
+    for (int32_t b = 0; b < B; ++b) {
+        if (b == 0 || share[b] == 0)
+            run0 = b;
+        const int32_t leader = run0 + (b - run0) / R * R;
+        /* members of the group led by `leader`: it and the next requests of
+           the same run (share != 0), at most R */
+        int32_t m = 1, Ls = 0;
+        while (m < R && leader + m < B && share[leader + m] != 0)
+            ++m;
+        if (m >= 2) {
+            Ls = share[leader + 1];
+            for (int32_t k = 2; k < m; ++k)
+                if (share[leader + k] < Ls)
+                    Ls = share[leader + k];
+        }
+        if (b == leader && m >= 2) {
+            item_req[I] = b;
+            item_start[I] = 0;
+            item_len[I] = Ls;
+            item_m[I] = m;
+            item_solo[I] = 0;
+            total += (Ls + T - 1) / T;
+            tiles_prefix[I + 1] = (int32_t)total;
+            ++I;
+        }
+        req_shared[b] = m >= 2 ? (int32_t)(I - 1 - (b - leader)) : -1;
+        req_member[b] = m >= 2 ? b - leader : 0;
+        /* the shared item of b's group was emitted at the leader, b - leader own
+           items ago: I - 1 - (b - leader) when b's own item is not yet counted */
+        item_req[I] = b;
+        item_start[I] = m >= 2 ? Ls : 0;
+        item_len[I] = Le[b] - (m >= 2 ? Ls : 0);
+        item_m[I] = 1;
+        item_solo[I] = m >= 2 ? 0 : 1;
+        req_own[b] = (int32_t)I;
+        total += ((int64_t)item_len[I] + T - 1) / T;
+        if (total > INT32_MAX) {
+            free(Le);
+            free(share);
+            return -4;
+        }
+        tiles_prefix[I + 1] = (int32_t)total;
+        ++I;
+    }
+    free(Le);
+    free(share);
+    /* 5. mode 0 over items */
+    const int64_t N = total * Hkv;
+    if (N > INT32_MAX)
+        return -4;
+    const int64_t We = N < W ? N : W;
+    int64_t nseg = 0;
+    seg_prefix[0] = 0;
+    for (int64_t i = 0; i < I; ++i) {
+        const int64_t ni = tiles_prefix[i + 1] - tiles_prefix[i];
+        for (int32_t g = 0; g < Hkv; ++g) {
+            const int64_t ig = i * Hkv + g;
+            if (ni == 0) {
+                first_wg[ig] = -1;
+            } else {
+                const int64_t u0 = (int64_t)tiles_prefix[i] * Hkv + g * ni;
+                const int64_t u1 = u0 + ni - 1;
+                const int64_t w0 = ((u0 + 1) * We - 1) / N;
+                const int64_t w1 = ((u1 + 1) * We - 1) / N;
+                first_wg[ig] = (int32_t)w0;
+                nseg += w1 - w0 + 1;
+            }
+            seg_prefix[ig + 1] = (int32_t)nseg;
+        }
+    }
+    for (int64_t w = 0; w <= W; ++w)
+        wg_begin[w] = (int32_t)(w <= We && We > 0 ? w * N / We : N);
+    int64_t i = 0;
+    for (int64_t w = 0; w < W; ++w) {
+        if (w >= We) {
+            wg_start[w] = (int32_t)I;
+            continue;
+        }
+        const int64_t u = wg_begin[w];
+        while (i < I && (int64_t)tiles_prefix[i + 1] * Hkv <= u)
+            ++i;
+        wg_start[w] = (int32_t)i;
+    }
+    const int32_t h[8] = {status, (int32_t)N, (int32_t)We, (int32_t)maxle, (int32_t)I, R, (int32_t)total, T};
+    memcpy(header, h, sizeof h);
+    return 0;
+}
+
 /*
  * The e4m3fn code nearest to the fp32 value y: ties to even, magnitudes at or
  * above 448 (the largest finite e4m3fn value) saturate to +-448, NaN gives the
