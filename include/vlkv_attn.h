@@ -61,6 +61,7 @@ extern "C" {
 /* mode */
 #define ATTN_DYNAMIC  0          /* balanced per-step tile plan */
 #define ATTN_STATIC   1          /* static split-K: S fixed splits per (request, kv head) */
+#define ATTN_SHARED   2          /* dynamic plan that reads prefix-shared pages once (see attn_plan) */
 
 /* status word bits (attn_get_status) */
 #define ATTN_STATUS_BAD_LENGTH  1u  /* some L_b < 0 or L_b > pt_stride * page_size: treated as 0 */
@@ -78,7 +79,7 @@ extern "C" {
  *   num_wgs        W, workgroups of the dynamic decode launch (>= 1); a good
  *                  value is 2 per compute unit (attn_device_cu_count)
  *   kv_dtype       ATTN_KV_BF16 or ATTN_KV_FP8_E4M3
- *   mode           ATTN_DYNAMIC or ATTN_STATIC
+ *   mode           ATTN_DYNAMIC, ATTN_STATIC or ATTN_SHARED
  *   static_splits  S for ATTN_STATIC (>= 1); 0 picks
  *                  clamp(ceil(num_wgs / (B*Hkv)), 1, ceil(pt_stride*P / T))
  */
@@ -122,7 +123,7 @@ int attn_device_cu_count(int device, int32_t *cus);
 /*
  * Build the tile plan for this step into the workspace (one small kernel).
  *   lengths    (device) int32 [B], current context length of each request
- *   page_table (device) int32 [B][pt_stride]; not read by the planner
+ *   page_table (device) int32 [B][pt_stride]; read only in ATTN_SHARED mode
  *   workspace  (device) >= attn_workspace_bytes(shape) bytes, 256-B aligned
  * Dynamic mode: the (request, kv head, tile) units are numbered request-major
  * and cut into num_wgs contiguous, equal (+-1) ranges; each maximal run of one
@@ -130,6 +131,18 @@ int attn_device_cu_count(int device, int32_t *cus);
  * Static mode: chunk = ceil(max L / S) rounded up to a multiple of
  * lcm(page_size, tile_tokens); split s of each (request, kv head) covers
  * tokens [s*chunk, min((s+1)*chunk, L_b)) and may be empty.
+ * Shared mode (prefix caching, which the article lists among the situations
+ * the kernels must handle [Tencent HPC lands in SGLang, challenging default
+ * inference kernels, sec. "Why Tencent HPC matters for online model
+ * serving"]): request b shares with b-1 the leading page slots that hold the
+ * same valid page id, capped by both lengths and rounded down to whole tiles.
+ * Runs of adjacent sharing requests are cut into groups of R = 16 / G
+ * (G = Hq/Hkv; one pass holds 16 query rows); a group of two or more reads its
+ * common prefix once, as one item whose query rows are the members' heads, and
+ * each request keeps an item for its remaining tokens. The partition above then
+ * runs over (item, kv head, tile) units. Results equal the other modes' up to
+ * the order of the softmax merge. The plan's arrays are over items
+ * (attn_read_plan, attn_read_plan_items).
  * The workspace contents stay valid until the next attn_plan on it.
  */
 int attn_plan(const attn_shape *shape, const int32_t *lengths, const int32_t *page_table,
@@ -185,7 +198,8 @@ int attn_workspace_init(const attn_shape *shape, void *workspace, size_t workspa
  * several workgroups merges the pair's partials by log-sum-exp weighting.
  *   lengths    (device) int32 [B], current context length of each request
  *   other arguments as in attn_decode; shape->mode selects the dynamic plan or
- *   the static split-K.
+ *   the static split-K. ATTN_SHARED is not fused: attn_step then enqueues
+ *   attn_plan, attn_decode and attn_combine (three launches).
  * The workspace must have been prepared by attn_workspace_init. The status word
  * is sticky: bits set by any step stay set until attn_workspace_init or
  * attn_plan rewrites it. Two attn_step calls on one workspace must not overlap
@@ -237,10 +251,31 @@ int attn_get_status(const void *workspace, uint32_t *flags, void *stream);
  * pointer may be NULL to skip that array. Sizes: header[8], len_eff[B],
  * tiles_prefix[B+1], seg_prefix[B*Hkv+1], first_wg[B*Hkv], wg_begin[W+1],
  * wg_start_b[W]. header = {status, N, W_eff, max L, chunk, S, total tiles, T}.
+ * ATTN_SHARED: the arrays are over items, not requests, with B replaced by 2B
+ * (the first header[4] items are used): len_eff = item token counts,
+ * wg_start_b = each range's first item; header = {status, N, W_eff, max L,
+ * number of items, R, total tiles, T}.
  */
 int attn_read_plan(const attn_shape *shape, const void *workspace, int32_t *header,
                    int32_t *len_eff, int32_t *tiles_prefix, int32_t *seg_prefix,
                    int32_t *first_wg, int32_t *wg_begin, int32_t *wg_start_b, void *stream);
+
+/*
+ * ATTN_SHARED only: copy the item description of the plan into host memory
+ * (synchronises `stream`); NULL skips an array. Sizes 2B for the item arrays,
+ * B for the request arrays; entries past header[4] items are unspecified.
+ *   item_req[i]   first request of item i (its page table row)
+ *   item_start[i] first token of item i within that request
+ *   item_m[i]     requests item i serves: item_req[i] .. + item_m[i] - 1
+ *   item_solo[i]  1 if item i is its request's only item
+ *   req_shared[b] the shared item of request b's group, or -1
+ *   req_member[b] b's position in that group (query rows member*G..)
+ *   req_own[b]    the item holding b's own tokens
+ */
+int attn_read_plan_items(const attn_shape *shape, const void *workspace, int32_t *item_req,
+                         int32_t *item_start, int32_t *item_m, int32_t *item_solo,
+                         int32_t *req_shared, int32_t *req_member, int32_t *req_own,
+                         void *stream);
 
 /* Text of the last error on the calling thread ("" if none). */
 const char *attn_last_error(void);

@@ -78,7 +78,7 @@ static int check(const attn_shape *s, Shape *out)
         return fail(ATTN_ERR_INVALID_ARG, "num_wgs %d outside [1, 2^20]", s->num_wgs);
     if (s->kv_dtype != ATTN_KV_BF16 && s->kv_dtype != ATTN_KV_FP8_E4M3)
         return fail(ATTN_ERR_UNSUPPORTED, "kv_dtype %d", s->kv_dtype);
-    if (s->mode != ATTN_DYNAMIC && s->mode != ATTN_STATIC)
+    if (s->mode != ATTN_DYNAMIC && s->mode != ATTN_STATIC && s->mode != ATTN_SHARED)
         return fail(ATTN_ERR_INVALID_ARG, "mode %d", s->mode);
     if (s->static_splits < 0)
         return fail(ATTN_ERR_INVALID_ARG, "static_splits %d < 0", s->static_splits);
@@ -86,7 +86,8 @@ static int check(const attn_shape *s, Shape *out)
     const int64_t max_tokens = (int64_t)s->pt_stride * s->page_size;
     if (max_tokens > INT32_MAX / 2)
         return fail(ATTN_ERR_INVALID_ARG, "pt_stride * page_size too large");
-    const int64_t max_units = (int64_t)s->batch * s->num_kv_heads * ceil_div(max_tokens, s->tile_tokens);
+    // (mode 2 splits a request into at most two items: one more tile each)
+    const int64_t max_units = (int64_t)s->batch * s->num_kv_heads * (ceil_div(max_tokens, s->tile_tokens) + 1);
     if (max_units > INT32_MAX / 2)
         return fail(ATTN_ERR_INVALID_ARG, "batch * kv heads * tiles per request too large");
     const int32_t S = s->mode == ATTN_STATIC ? effective_splits(s) : 0;
@@ -112,19 +113,35 @@ WsLayout ws_layout(const Shape &s)
         return at;
     };
     const int64_t nbg = (int64_t)s.B * s.Hkv;
-    // dynamic: at most W_eff + B*Hkv segments with attn_plan's slots, and two
-    // slots per workgroup (its first and last segment) in the single launch
-    L.max_slots = s.mode == ATTN_STATIC ? nbg * s.S : nbg + 2 * (int64_t)s.W;
+    const bool shared = s.mode == ATTN_SHARED;
+    // the plan's "items": requests, or in mode 2 up to two per request
+    L.max_items = shared ? 2 * (int64_t)s.B : s.B;
+    const int64_t nig = L.max_items * s.Hkv;
+    // dynamic: at most W_eff + (item, kv head) pairs segments with attn_plan's
+    // slots, and two slots per workgroup (its first and last segment) in the
+    // single launch
+    L.max_slots = s.mode == ATTN_STATIC ? nbg * s.S : nig + 2 * (int64_t)s.W;
+    L.slot_rows = shared ? shared_group(s.G) * s.G : s.G;
     L.header = take(sizeof(int32_t) * kHeaderInts);
-    L.len_eff = take(sizeof(int32_t) * s.B);
-    L.tiles_prefix = take(sizeof(int32_t) * (s.B + 1));
-    L.seg_prefix = take(sizeof(int32_t) * (nbg + 1));
-    L.first_wg = take(sizeof(int32_t) * nbg);
+    L.len_eff = take(sizeof(int32_t) * L.max_items);
+    L.tiles_prefix = take(sizeof(int32_t) * (L.max_items + 1));
+    L.seg_prefix = take(sizeof(int32_t) * (nig + 1));
+    L.first_wg = take(sizeof(int32_t) * nig);
     L.wg_begin = take(sizeof(int32_t) * (s.W + 1));
     L.wg_start_b = take(sizeof(int32_t) * s.W);
+    const int64_t ni = shared ? L.max_items : 0, nr = shared ? s.B : 0;
+    L.item_req = take(sizeof(int32_t) * ni);
+    L.item_start = take(sizeof(int32_t) * ni);
+    L.item_m = take(sizeof(int32_t) * ni);
+    L.item_solo = take(sizeof(int32_t) * ni);
+    L.req_shared = take(sizeof(int32_t) * nr);
+    L.req_member = take(sizeof(int32_t) * nr);
+    L.req_own = take(sizeof(int32_t) * nr);
+    L.share = take(sizeof(int32_t) * nr);
+    L.len_req = take(sizeof(int32_t) * nr);
     L.counters = take(sizeof(int32_t) * nbg);
-    L.part_lse = take(sizeof(float) * L.max_slots * s.G);
-    L.part_o = take(sizeof(float) * L.max_slots * s.G * s.D);
+    L.part_lse = take(sizeof(float) * L.max_slots * L.slot_rows);
+    L.part_o = take(sizeof(float) * L.max_slots * L.slot_rows * s.D);
     L.total = off;
     return L;
 }
@@ -197,10 +214,18 @@ int attn_device_cu_count(int device, int32_t *cus)
     return ok();
 }
 
+static int enqueue_plan(const Shape &s, const WsLayout &L, const int32_t *lengths, const int32_t *page_table,
+                        void *workspace, hipStream_t st);
+static int enqueue_decode(const Shape &s, const WsLayout &L, const void *q, const void *k_cache,
+                          const void *v_cache, const float *k_scale, const float *v_scale,
+                          const int32_t *page_table, float sm_scale, void *workspace, void *out, float *lse,
+                          hipStream_t st);
+static int enqueue_combine(const Shape &s, const WsLayout &L, const void *workspace, void *out, float *lse,
+                           hipStream_t st);
+
 int attn_plan(const attn_shape *shape, const int32_t *lengths, const int32_t *page_table,
               void *workspace, size_t workspace_bytes, void *stream)
 {
-    (void)page_table;
     Shape s;
     WsLayout L;
     int rc = check(shape, &s);
@@ -208,10 +233,19 @@ int attn_plan(const attn_shape *shape, const int32_t *lengths, const int32_t *pa
         return rc;
     if (!lengths)
         return fail(ATTN_ERR_INVALID_ARG, "lengths is NULL");
+    if (s.mode == ATTN_SHARED && !page_table)
+        return fail(ATTN_ERR_INVALID_ARG, "mode ATTN_SHARED needs the page table");
     if ((rc = check_ws(s, workspace, workspace_bytes, &L)) != ATTN_OK)
         return rc;
-    PlanArgs a;
+    return enqueue_plan(s, L, lengths, page_table, workspace, static_cast<hipStream_t>(stream));
+}
+
+static int enqueue_plan(const Shape &s, const WsLayout &L, const int32_t *lengths, const int32_t *page_table,
+                        void *workspace, hipStream_t st)
+{
+    PlanArgs a{};
     a.lengths = lengths;
+    a.page_table = page_table;
     a.header = at<int32_t>(workspace, L.header);
     a.len_eff = at<int32_t>(workspace, L.len_eff);
     a.tiles_prefix = at<int32_t>(workspace, L.tiles_prefix);
@@ -219,15 +253,26 @@ int attn_plan(const attn_shape *shape, const int32_t *lengths, const int32_t *pa
     a.first_wg = at<int32_t>(workspace, L.first_wg);
     a.wg_begin = at<int32_t>(workspace, L.wg_begin);
     a.wg_start_b = at<int32_t>(workspace, L.wg_start_b);
+    a.item_req = at<int32_t>(workspace, L.item_req);
+    a.item_start = at<int32_t>(workspace, L.item_start);
+    a.item_m = at<int32_t>(workspace, L.item_m);
+    a.item_solo = at<int32_t>(workspace, L.item_solo);
+    a.req_shared = at<int32_t>(workspace, L.req_shared);
+    a.req_member = at<int32_t>(workspace, L.req_member);
+    a.req_own = at<int32_t>(workspace, L.req_own);
+    a.share = at<int32_t>(workspace, L.share);
+    a.len_req = at<int32_t>(workspace, L.len_req);
     a.B = s.B;
     a.Hkv = s.Hkv;
+    a.G = s.G;
     a.P = s.P;
     a.pt_stride = s.pt_stride;
+    a.num_pages = s.num_pages;
     a.T = s.T;
     a.W = s.W;
     a.mode = s.mode;
     a.S = s.S;
-    const hipError_t e = launch_plan(a, static_cast<hipStream_t>(stream));
+    const hipError_t e = launch_plan(a, st);
     if (e != hipSuccess)
         return hip_fail(e, "plan launch");
     return ok();
@@ -254,7 +299,16 @@ int attn_decode(const attn_shape *shape, const void *q, const void *k_cache, con
         return fail(ATTN_ERR_INVALID_ARG, "q, caches and out must be 16-byte aligned");
     if ((rc = check_ws(s, workspace, workspace_bytes, &L)) != ATTN_OK)
         return rc;
-    DecodeArgs a;
+    return enqueue_decode(s, L, q, k_cache, v_cache, k_scale, v_scale, page_table, sm_scale, workspace, out, lse,
+                          static_cast<hipStream_t>(stream));
+}
+
+static int enqueue_decode(const Shape &s, const WsLayout &L, const void *q, const void *k_cache,
+                          const void *v_cache, const float *k_scale, const float *v_scale,
+                          const int32_t *page_table, float sm_scale, void *workspace, void *out, float *lse,
+                          hipStream_t st)
+{
+    DecodeArgs a{};
     a.lengths = nullptr;
     a.counters = nullptr;
     a.q = static_cast<const uint16_t *>(q);
@@ -270,6 +324,10 @@ int attn_decode(const attn_shape *shape, const void *q, const void *k_cache, con
     a.first_wg = at<int32_t>(workspace, L.first_wg);
     a.wg_begin = at<int32_t>(workspace, L.wg_begin);
     a.wg_start_b = at<int32_t>(workspace, L.wg_start_b);
+    a.item_req = at<int32_t>(workspace, L.item_req);
+    a.item_start = at<int32_t>(workspace, L.item_start);
+    a.item_m = at<int32_t>(workspace, L.item_m);
+    a.item_solo = at<int32_t>(workspace, L.item_solo);
     a.part_o = at<float>(workspace, L.part_o);
     a.part_lse = at<float>(workspace, L.part_lse);
     a.out = static_cast<uint16_t *>(out);
@@ -285,10 +343,11 @@ int attn_decode(const attn_shape *shape, const void *q, const void *k_cache, con
     a.S = s.S;
     a.T = s.T;
     a.W = s.W;
+    a.slot_rows = L.slot_rows;
     a.scale_log2 = sm_scale * 1.4426950408889634f;
     const int grid = s.mode == ATTN_STATIC ? s.B * s.Hkv * s.S : s.W;
-    const hipError_t e = launch_decode(a, s.mode == ATTN_STATIC ? SRC_STATIC : SRC_DYNAMIC, s.kv_fp8, grid,
-                                       static_cast<hipStream_t>(stream));
+    const int src = s.mode == ATTN_STATIC ? SRC_STATIC : s.mode == ATTN_SHARED ? SRC_SHARED : SRC_DYNAMIC;
+    const hipError_t e = launch_decode(a, src, s.kv_fp8, grid, st);
     if (e != hipSuccess)
         return hip_fail(e, "decode launch");
     return ok();
@@ -308,8 +367,18 @@ int attn_combine(const attn_shape *shape, const void *workspace, size_t workspac
         return fail(ATTN_ERR_INVALID_ARG, "out must be 16-byte aligned");
     if ((rc = check_ws(s, workspace, workspace_bytes, &L)) != ATTN_OK)
         return rc;
-    CombineArgs a;
+    return enqueue_combine(s, L, workspace, out, lse, static_cast<hipStream_t>(stream));
+}
+
+static int enqueue_combine(const Shape &s, const WsLayout &L, const void *workspace, void *out, float *lse,
+                           hipStream_t st)
+{
+    CombineArgs a{};
     a.header = at<int32_t>(workspace, L.header);
+    a.req_shared = at<int32_t>(workspace, L.req_shared);
+    a.req_member = at<int32_t>(workspace, L.req_member);
+    a.req_own = at<int32_t>(workspace, L.req_own);
+    a.item_solo = at<int32_t>(workspace, L.item_solo);
     a.seg_prefix = at<int32_t>(workspace, L.seg_prefix);
     a.part_o = at<float>(workspace, L.part_o);
     a.part_lse = at<float>(workspace, L.part_lse);
@@ -321,7 +390,8 @@ int attn_combine(const attn_shape *shape, const void *workspace, size_t workspac
     a.G = s.G;
     a.mode = s.mode;
     a.S = s.S;
-    const hipError_t e = launch_combine(a, static_cast<hipStream_t>(stream));
+    a.slot_rows = L.slot_rows;
+    const hipError_t e = launch_combine(a, st);
     if (e != hipSuccess)
         return hip_fail(e, "combine launch");
     return ok();
@@ -364,6 +434,17 @@ int attn_step(const attn_shape *shape, const void *q, const void *k_cache, const
         return fail(ATTN_ERR_INVALID_ARG, "q, caches and out must be 16-byte aligned");
     if ((rc = check_ws(s, workspace, workspace_bytes, &L)) != ATTN_OK)
         return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (s.mode == ATTN_SHARED) {
+        // the prefix-shared plan groups requests by comparing page tables; it
+        // runs as its own launch, followed by the decode and the combine
+        if ((rc = enqueue_plan(s, L, lengths, page_table, workspace, st)) != ATTN_OK)
+            return rc;
+        if ((rc = enqueue_decode(s, L, q, k_cache, v_cache, k_scale, v_scale, page_table, sm_scale, workspace, out,
+                                 lse, st)) != ATTN_OK)
+            return rc;
+        return enqueue_combine(s, L, workspace, out, lse, st);
+    }
     DecodeArgs a{};
     a.lengths = lengths;
     a.counters = at<int32_t>(workspace, L.counters);
@@ -389,10 +470,11 @@ int attn_step(const attn_shape *shape, const void *q, const void *k_cache, const
     a.S = s.S;
     a.T = s.T;
     a.W = s.W;
+    a.slot_rows = L.slot_rows;
     a.scale_log2 = sm_scale * 1.4426950408889634f;
     const int grid = s.mode == ATTN_STATIC ? s.B * s.Hkv * s.S : s.W;
     const hipError_t e = launch_decode(a, s.mode == ATTN_STATIC ? SRC_FUSED_STATIC : SRC_FUSED_DYNAMIC,
-                                       s.kv_fp8, grid, static_cast<hipStream_t>(stream));
+                                       s.kv_fp8, grid, st);
     if (e != hipSuccess)
         return hip_fail(e, "step launch");
     return ok();
@@ -467,16 +549,54 @@ int attn_read_plan(const attn_shape *shape, const void *workspace, int32_t *head
         return fail(ATTN_ERR_INVALID_ARG, "workspace is NULL");
     const WsLayout L = ws_layout(s);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const int64_t nbg = (int64_t)s.B * s.Hkv;
+    const int64_t ni = L.max_items, nig = L.max_items * s.Hkv;
     struct Item {
         int32_t *dst;
         size_t off;
         int64_t n;
     } items[] = {
-        {header, L.header, kHeaderInts},      {len_eff, L.len_eff, s.B},
-        {tiles_prefix, L.tiles_prefix, s.B + 1}, {seg_prefix, L.seg_prefix, nbg + 1},
-        {first_wg, L.first_wg, nbg},           {wg_begin, L.wg_begin, s.W + 1},
+        {header, L.header, kHeaderInts},      {len_eff, L.len_eff, ni},
+        {tiles_prefix, L.tiles_prefix, ni + 1}, {seg_prefix, L.seg_prefix, nig + 1},
+        {first_wg, L.first_wg, nig},           {wg_begin, L.wg_begin, s.W + 1},
         {wg_start_b, L.wg_start_b, s.W},
+    };
+    for (const Item &it : items) {
+        if (!it.dst)
+            continue;
+        const hipError_t e = hipMemcpyAsync(it.dst, at<int32_t>(workspace, it.off),
+                                            sizeof(int32_t) * it.n, hipMemcpyDeviceToHost, st);
+        if (e != hipSuccess)
+            return hip_fail(e, "plan copy");
+    }
+    const hipError_t e = hipStreamSynchronize(st);
+    if (e != hipSuccess)
+        return hip_fail(e, "plan copy sync");
+    return ok();
+}
+
+int attn_read_plan_items(const attn_shape *shape, const void *workspace, int32_t *item_req, int32_t *item_start,
+                         int32_t *item_m, int32_t *item_solo, int32_t *req_shared, int32_t *req_member,
+                         int32_t *req_own, void *stream)
+{
+    Shape s;
+    int rc = check(shape, &s);
+    if (rc != ATTN_OK)
+        return rc;
+    if (s.mode != ATTN_SHARED)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_read_plan_items needs mode ATTN_SHARED");
+    if (!workspace)
+        return fail(ATTN_ERR_INVALID_ARG, "workspace is NULL");
+    const WsLayout L = ws_layout(s);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    struct Item {
+        int32_t *dst;
+        size_t off;
+        int64_t n;
+    } items[] = {
+        {item_req, L.item_req, L.max_items},     {item_start, L.item_start, L.max_items},
+        {item_m, L.item_m, L.max_items},         {item_solo, L.item_solo, L.max_items},
+        {req_shared, L.req_shared, s.B},         {req_member, L.req_member, s.B},
+        {req_own, L.req_own, s.B},
     };
     for (const Item &it : items) {
         if (!it.dst)

@@ -145,21 +145,38 @@ struct Meta {
     int nseg;    // single launch: segments of the pair (arrivals before its merge)
     int wfirst;  // single launch, dynamic: workgroup of the pair's first segment
     int first_off;  // single launch, dynamic: slot offset of that first segment
+    int m;       // query requests b, b+1, .., b+m-1 (more than one: a shared prefix)
+    int tbase;   // first token of the item (0 unless a request's own rest)
     float ksc, vsc;
 };
 
-// Walks a workgroup's blocks in order. SRC_DYNAMIC / SRC_FUSED_DYNAMIC: the
-// contiguous unit range of the plan; SRC_STATIC / SRC_FUSED_STATIC: the one
+// Walks a workgroup's blocks in order. SRC_DYNAMIC / SRC_FUSED_DYNAMIC /
+// SRC_SHARED: the contiguous unit range of the plan (SRC_SHARED: over items,
+// b is then the item index); SRC_STATIC / SRC_FUSED_STATIC: the one
 // (b, g, split) of this workgroup.
 template <int SRC>
 struct Walker {
     static constexpr bool kFused = SRC == SRC_FUSED_DYNAMIC || SRC == SRC_FUSED_STATIC;
-    static constexpr bool kDyn = SRC == SRC_DYNAMIC || SRC == SRC_FUSED_DYNAMIC;
+    static constexpr bool kShared = SRC == SRC_SHARED;
+    static constexpr bool kPlanned = SRC == SRC_DYNAMIC || kShared;   // ranges from attn_plan's arrays
+    static constexpr bool kDyn = kPlanned || SRC == SRC_FUSED_DYNAMIC;
 
     const DecodeArgs *a;
     int w, wave;
     int b, g, blk, blk0, blk_end, L, nt, units_left, done;
     int slot, direct, nseg, wfirst, first_off;
+    // SRC_SHARED: the item's first request, first token, request count and
+    // whether it is its request's only item
+    int req = 0, ist = 0, mm = 1, solo = 1;
+    __device__ void load_item()
+    {
+        if (kShared) {
+            req = ldc(a->item_req, b);
+            ist = ldc(a->item_start, b);
+            mm = ldc(a->item_m, b);
+            solo = ldc(a->item_solo, b);
+        }
+    }
     // single launch, dynamic
     int tpb;                 // tiles before request b
     int first_seg;           // the next segment entered is the workgroup's first
@@ -193,11 +210,12 @@ struct Walker {
         const int nblk = (L + kBlockTokens - 1) / kBlockTokens;
         blk_end = min(tb * R, nblk);
         const int bg = b * a->Hkv + g;
-        if (SRC == SRC_DYNAMIC) {
+        if (kPlanned) {
             const int s0 = ldc(a->seg_prefix, bg);
             const int s1 = ldc(a->seg_prefix, bg + 1);
             slot = s0 + (w - ldc(a->first_wg, bg));
-            direct = (s1 - s0) == 1;
+            // an item that is not its request's only item always leaves a partial
+            direct = (s1 - s0) == 1 && solo;
         } else {
             // slot 2w for the workgroup's first segment, 2w+1 for its last; a
             // segment that is neither covers its whole pair and is direct
@@ -231,12 +249,13 @@ struct Walker {
         first_off = 0;
         if (kDyn) {
             int u0, u1;
-            if (SRC == SRC_DYNAMIC) {
+            if (kPlanned) {
                 u0 = ldc(a->wg_begin, w);
                 u1 = ldc(a->wg_begin, w + 1);
                 b = ldc(a->wg_start_b, w);
                 tpb = ldc(a->tiles_prefix, b);
                 nt = ldc(a->tiles_prefix, b + 1) - tpb;
+                load_item();
             } else {
                 N = N_;
                 We = We_;
@@ -299,6 +318,7 @@ struct Walker {
             nt = tiles_of(b);
         } while (nt == 0);
         L = length_of(b);
+        load_item();
     }
 
     // Number of blocks this workgroup will process (a scalar walk over its
@@ -343,6 +363,10 @@ struct Walker {
         m.nseg = nseg;
         m.wfirst = wfirst;
         m.first_off = first_off;
+        m.m = kShared ? mm : 1;
+        m.tbase = kShared ? ist : 0;
+        if (kShared)
+            m.b = req;
         m.ksc = 1.f;
         m.vsc = 1.f;
         if (done)
@@ -429,11 +453,12 @@ __device__ __forceinline__ void merge_write(float M, float den, f32x4 o, uint16_
 }
 
 // Merge n partials of one (request, kv head) pair into the bf16 output and the
-// natural-log lse. slot_of(s) gives the slot of the s-th partial. Run by all
-// threads of a workgroup. COHERENT reads the partials with agent-scope loads
-// (partials written in the same launch).
-template <bool COHERENT, typename SlotOf>
-__device__ __forceinline__ void merge_partials(const float *part_o, const float *part_lse, int n, SlotOf slot_of,
+// natural-log lse. base_of(s) is the partial row of head 0 of the s-th partial
+// (its heads are the G rows from there). Run by all threads of a workgroup.
+// COHERENT reads the partials with agent-scope loads (partials written in the
+// same launch).
+template <bool COHERENT, typename BaseOf>
+__device__ __forceinline__ void merge_partials(const float *part_o, const float *part_lse, int n, BaseOf base_of,
                                                int G, int Hq, int b, int g, uint16_t *out, float *lse)
 {
     constexpr int D = kHeadDim;
@@ -447,7 +472,7 @@ __device__ __forceinline__ void merge_partials(const float *part_o, const float 
             f32x4 xs[kMergeBatch];
 #pragma unroll
             for (int j = 0; j < kMergeBatch; ++j) {
-                const size_t sl = (size_t)slot_of(s0 + j < n ? s0 + j : s0) * G + h;
+                const size_t sl = (size_t)base_of(s0 + j < n ? s0 + j : s0) + h;
                 ls[j] = ld(part_lse + sl);
                 const float *po = part_o + sl * D + d4;
                 if (COHERENT)
@@ -474,6 +499,7 @@ struct DecodeLds {
     float e[kWaves][kMaxGroup];
     int red[2 * kWaves];
     int flag;
+    float vs[kMaxGroup];   // SRC_SHARED: V scale of each query row
 };
 
 template <int SRC, int KVFP8>
@@ -481,7 +507,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
 {
     constexpr bool kFused = SRC == SRC_FUSED_DYNAMIC || SRC == SRC_FUSED_STATIC;
     const int w = blockIdx.x;
-    if (SRC == SRC_DYNAMIC && w >= ldc(a.header, H_WEFF))
+    if ((SRC == SRC_DYNAMIC || SRC == SRC_SHARED) && w >= ldc(a.header, H_WEFF))
         return;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -613,17 +639,29 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
             // q of (b, g) as the B operand: head = row. Branch-free: rows >= G
             // read head 0 and are zeroed when copied at the segment's first block,
             // so nothing here waits for the load and no divergent control flow
-            // separates the scalar bookkeeping of the pipeline.
-            const int hrow = row < G ? row : 0;
-            const uint16_t *qp = a.q + ((size_t)mt.b * a.Hq + (size_t)mt.g * G + hrow) * D;
+            // separates the scalar bookkeeping of the pipeline. A shared prefix
+            // (m requests) stacks them: row r is head r % G of request b + r / G.
+            const int hrow = row < mt.m * G ? row : 0;
+            int qb = mt.b, qh = hrow;
+            if (SRC == SRC_SHARED) {
+                const int mem = hrow / G;
+                qb += mem;
+                qh = hrow - mem * G;
+            }
+            const uint16_t *qp = a.q + ((size_t)qb * a.Hq + (size_t)mt.g * G + qh) * D;
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 const int d0 = KVFP8 ? 16 * grp + 64 * (kk >> 1) + 8 * (kk & 1) : 32 * kk + 8 * grp;
                 s.q[kk] = *reinterpret_cast<const u32x4 *>(qp + d0);  // zeroed at use
             }
             if (KVFP8) {
-                mt.ksc = ldc(a.k_scale, (size_t)mt.b * a.Hkv + mt.g);
-                mt.vsc = ldc(a.v_scale, (size_t)mt.b * a.Hkv + mt.g);
+                if (SRC == SRC_SHARED) {   // per row: the scales of the row's request
+                    mt.ksc = a.k_scale[(size_t)qb * a.Hkv + mt.g];
+                    mt.vsc = a.v_scale[(size_t)qb * a.Hkv + mt.g];
+                } else {
+                    mt.ksc = ldc(a.k_scale, (size_t)mt.b * a.Hkv + mt.g);
+                    mt.vsc = ldc(a.v_scale, (size_t)mt.b * a.Hkv + mt.g);
+                }
             }
         }
         // The slab address is wave-uniform (scalar registers); each lane adds its
@@ -631,12 +669,13 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
         // 64-bit address arithmetic runs per lane.
         size_t slab = (size_t)mt.g * page_head_bytes;   // page 0 of kv head g
         if (mt.valid && mt.nv > 0) {
-            const int page = ldc(a.page_table, (size_t)mt.b * a.pt_stride + mt.tok0 / a.P);
+            const int tok = mt.tbase + mt.tok0;   // token index in the request
+            const int page = ldc(a.page_table, (size_t)mt.b * a.pt_stride + tok / a.P);
             if (page < 0 || page >= a.num_pages) {
                 bad_page = 1;   // reported once at the end of the kernel
                 mt.nv = 0;
             } else {
-                slab = ((size_t)page * a.Hkv + mt.g) * page_head_bytes + (size_t)(mt.tok0 % a.P) * (D * EB);
+                slab = ((size_t)page * a.Hkv + mt.g) * page_head_bytes + (size_t)(tok % a.P) * (D * EB);
             }
         }
         if (!mt.valid)
@@ -663,11 +702,14 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
     auto finish = [&](const Meta &mt) {
         const float l_tot = xsum4(l_run);
         const float e_tot = xsum4(e_run);
-        if (row < G) {
+        const int rows = mt.m * G;   // query rows of this segment
+        if (row < rows) {
             if (grp == 0) {
                 lds.m[wave][row] = m_run;
                 lds.l[wave][row] = l_tot;
                 lds.e[wave][row] = e_tot;
+                if (SRC == SRC_SHARED && wave == 0)
+                    lds.vs[row] = vsc_run;   // per row: its request's V scale
             }
 #pragma unroll
             for (int mb = 0; mb < 8; ++mb) {
@@ -682,7 +724,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
         }
         __syncthreads();
         const int tid = threadIdx.x;
-        for (int idx = tid; idx < G * 32; idx += kDecodeThreads) {
+        for (int idx = tid; idx < rows * 32; idx += kDecodeThreads) {
             const int h = idx >> 5, d4 = (idx & 31) * 4;
             float M = -INFINITY;
 #pragma unroll
@@ -700,27 +742,29 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
                     const f32x4 x = *reinterpret_cast<const f32x4 *>(&lds.acc[v][h][d4]);
                     o += e * x;
                 }
-                const float r = vsc_run / den;
+                const float r = (SRC == SRC_SHARED ? lds.vs[h] : vsc_run) / den;
                 o *= r;
                 lse2 = M + log2f(ex);
             }
-            const size_t hq = (size_t)mt.b * a.Hq + (size_t)mt.g * G + h;
+            const int mem = SRC == SRC_SHARED ? h / G : 0;   // row h: head h % G of request b + h / G
+            const size_t hq = (size_t)(mt.b + mem) * a.Hq + (size_t)mt.g * G + (h - mem * G);
+            const size_t prow = (size_t)mt.slot * a.slot_rows + h;   // partial row
             if (mt.direct) {
                 const bf16x4 ob = __builtin_convertvector(o, bf16x4);
                 *reinterpret_cast<bf16x4 *>(a.out + hq * D + d4) = ob;
                 if (a.lse && d4 == 0)
                     a.lse[hq] = lse2 * kLn2;
             } else if (kFused) {
-                float *po = a.part_o + ((size_t)mt.slot * G + h) * D + d4;
+                float *po = a.part_o + prow * D + d4;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     store_coherent(po + i, o[i]);
                 if (d4 == 0)
-                    store_coherent(a.part_lse + (size_t)mt.slot * G + h, lse2);
+                    store_coherent(a.part_lse + prow, lse2);
             } else {
-                *reinterpret_cast<f32x4 *>(a.part_o + ((size_t)mt.slot * G + h) * D + d4) = o;
+                *reinterpret_cast<f32x4 *>(a.part_o + prow * D + d4) = o;
                 if (d4 == 0)
-                    a.part_lse[(size_t)mt.slot * G + h] = lse2;
+                    a.part_lse[prow] = lse2;
             }
         }
         if (kFused && !mt.direct) {
@@ -741,14 +785,15 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
             }
             __syncthreads();
             if (lds.flag) {
+                const int sr = a.slot_rows;
                 if (SRC == SRC_FUSED_DYNAMIC) {
                     const int wf = mt.wfirst, off = mt.first_off;
                     merge_partials<true>(a.part_o, a.part_lse, mt.nseg,
-                                         [=](int s) { return 2 * (wf + s) + (s == 0 ? off : 0); },
+                                         [=](int s) { return (2 * (wf + s) + (s == 0 ? off : 0)) * sr; },
                                          G, a.Hq, mt.b, mt.g, a.out, a.lse);
                 } else {
                     const int s0 = bg * a.S;
-                    merge_partials<true>(a.part_o, a.part_lse, mt.nseg, [=](int s) { return s0 + s; },
+                    merge_partials<true>(a.part_o, a.part_lse, mt.nseg, [=](int s) { return (s0 + s) * sr; },
                                          G, a.Hq, mt.b, mt.g, a.out, a.lse);
                 }
             }
@@ -764,7 +809,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
         if (mt.first) {
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
-                qreg[kk] = row < G ? s.q[kk] : u32x4{0u, 0u, 0u, 0u};
+                qreg[kk] = row < mt.m * G ? s.q[kk] : u32x4{0u, 0u, 0u, 0u};
             m_run = -INFINITY;
             l_run = 0.f;
             e_run = 0.f;
@@ -897,8 +942,31 @@ __global__ __launch_bounds__(kDecodeThreads) void combine_kernel(CombineArgs a)
     }
     if (n == 1)
         return;
-    merge_partials<false>(a.part_o, a.part_lse, n, [=](int s) { return s0 + s; }, a.G, a.Hq, b, g, a.out,
+    const int sr = a.slot_rows;
+    merge_partials<false>(a.part_o, a.part_lse, n, [=](int s) { return (s0 + s) * sr; }, a.G, a.Hq, b, g, a.out,
                           a.lse);
+}
+
+// Mode 2: one workgroup per (request, kv head). The request's partials are
+// those of its group's shared item (rows member*G..) followed by those of its
+// own item; a solo item with one segment was written directly by the decode.
+__global__ __launch_bounds__(kDecodeThreads) void combine_shared_kernel(CombineArgs a)
+{
+    const int bg = blockIdx.x;
+    const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+    const int io = a.req_own[b], is = a.req_shared[b];
+    const int o0 = a.seg_prefix[io * a.Hkv + g], no = a.seg_prefix[io * a.Hkv + g + 1] - o0;
+    if (a.item_solo[io] && no == 1)
+        return;
+    int s0 = 0, ns = 0;
+    if (is >= 0) {
+        s0 = a.seg_prefix[is * a.Hkv + g];
+        ns = a.seg_prefix[is * a.Hkv + g + 1] - s0;
+    }
+    const int sr = a.slot_rows, off = a.req_member[b] * a.G;
+    merge_partials<false>(a.part_o, a.part_lse, ns + no,
+                          [=](int s) { return s < ns ? (s0 + s) * sr + off : (o0 + s - ns) * sr; }, a.G, a.Hq, b,
+                          g, a.out, a.lse);
 }
 
 // Clears the status word and the arrival counters of a workspace.
@@ -927,6 +995,8 @@ hipError_t launch_decode(const DecodeArgs &a, int src, int kv_fp8, int grid, hip
     case 5: VLKV_LAUNCH(SRC_FUSED_DYNAMIC, 1); break;
     case 6: VLKV_LAUNCH(SRC_FUSED_STATIC, 0); break;
     case 7: VLKV_LAUNCH(SRC_FUSED_STATIC, 1); break;
+    case 8: VLKV_LAUNCH(SRC_SHARED, 0); break;
+    case 9: VLKV_LAUNCH(SRC_SHARED, 1); break;
     default: return hipErrorInvalidValue;
     }
 #undef VLKV_LAUNCH
@@ -938,7 +1008,10 @@ hipError_t launch_combine(const CombineArgs &a, hipStream_t st)
     const int grid = a.B * a.Hkv;
     if (grid <= 0)
         return hipSuccess;
-    hipLaunchKernelGGL(combine_kernel, dim3(grid), dim3(kDecodeThreads), 0, st, a);
+    if (a.mode == MODE_SHARED)
+        hipLaunchKernelGGL(combine_shared_kernel, dim3(grid), dim3(kDecodeThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL(combine_kernel, dim3(grid), dim3(kDecodeThreads), 0, st, a);
     return hipGetLastError();
 }
 

@@ -17,9 +17,19 @@
 //   static  chunk C = ceil(max Le / S) rounded up to lcm(P, T); split s of a
 //           pair covers tokens [s*C, min((s+1)*C, Le_b)); slot = bg*S + s
 //
+//   shared  (mode 2) requests whose page tables begin with the same valid
+//           pages are grouped (runs of adjacent sharers cut into groups of
+//           R = 16 / G); a group reads its common prefix once as one "item"
+//           whose query rows are the members' heads, and each request keeps
+//           an item for the rest of its tokens. The partition above then runs
+//           over (item, g, t) units. Prefix caching is on the article's list
+//           of situations the kernels must handle [same page, same section,
+//           production-reliability paragraph].
+//
 // The work is O(B*Hkv + W) and latency-bound: each thread owns a contiguous
 // chunk of every array, so a prefix sum is one serial pass per thread, one
-// wave scan and one exchange of 4 wave totals through LDS.
+// wave scan and one exchange of 4 wave totals through LDS. Mode 2 adds the
+// page-table comparison of adjacent requests, 16 slots per dependent step.
 #include "vlkv_device.hpp"
 #include "vlkv_internal.hpp"
 
@@ -28,6 +38,85 @@ namespace {
 
 constexpr int kPT = 256;  // planner threads
 constexpr int kPW = kPT / 64;
+
+// The dynamic partition over n "items" (requests in modes 0, items in mode
+// 2) whose tiles prefix is tp[0..n]: segments of each (item, kv head) pair and
+// their prefix, each workgroup's range and first item, and the header.
+__device__ void plan_partition(const PlanArgs &a, const int32_t *tp, int n, int total, int status, int maxle,
+                               int h4, int h5, int *scan_lds)
+{
+    const int tid = threadIdx.x;
+    int run;
+    // segments per (item, g) and their prefix
+    const int nbg = n * a.Hkv;
+    const int64_t N = (int64_t)total * a.Hkv;
+    const int64_t We = N < a.W ? N : a.W;
+    const int cB = (nbg + kPT - 1) / kPT;
+    const int g0 = min(nbg, tid * cB), g1 = min(nbg, g0 + cB);
+    int segs = 0;
+    for (int bg = g0; bg < g1; ++bg) {
+        const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+        const int64_t nb = tp[b + 1] - tp[b];
+        if (nb == 0) {
+            a.first_wg[bg] = -1;
+        } else {
+            const int64_t u0 = (int64_t)tp[b] * a.Hkv + g * nb;
+            const int64_t w0 = div_floor((u0 + 1) * We - 1, N);
+            const int64_t w1 = div_floor((u0 + nb) * We - 1, N);
+            a.first_wg[bg] = (int32_t)w0;
+            segs += (int)(w1 - w0 + 1);
+        }
+    }
+    int nseg;
+    run = block_excl_scan<kPT>(segs, scan_lds, &nseg);
+    for (int bg = g0; bg < g1; ++bg) {
+        const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+        const int64_t nb = tp[b + 1] - tp[b];
+        if (nb) {
+            const int64_t u0 = (int64_t)tp[b] * a.Hkv + g * nb;
+            run += (int)(div_floor((u0 + nb) * We - 1, N) - div_floor((u0 + 1) * We - 1, N) + 1);
+        }
+        a.seg_prefix[bg + 1] = run;
+    }
+    if (tid == 0)
+        a.seg_prefix[0] = 0;
+
+    // 3) workgroup ranges and the request of each range's first unit
+    const int cC = (a.W + 1 + kPT - 1) / kPT;
+    const int w0 = min(a.W + 1, tid * cC), w1 = min(a.W + 1, w0 + cC);
+    int sb = 0;
+    if (w0 < w1 && We > 0) {
+        // largest item i in [0, n) with Hkv * tp[i] <= begin(w0)
+        const int64_t begin = w0 <= We ? div_floor((int64_t)w0 * N, We) : N;
+        int lo = 0, hi = n - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if ((int64_t)tp[mid] * a.Hkv <= begin)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        sb = lo;
+    }
+    for (int w = w0; w < w1; ++w) {
+        const int64_t begin = (w <= We && We > 0) ? div_floor((int64_t)w * N, We) : N;
+        a.wg_begin[w] = (int32_t)begin;
+        if (w < a.W) {
+            if (w < We) {
+                while (sb + 1 < n && (int64_t)tp[sb + 1] * a.Hkv <= begin)
+                    ++sb;
+                a.wg_start_b[w] = sb;
+            } else {
+                a.wg_start_b[w] = n;
+            }
+        }
+    }
+    if (tid == 0) {
+        const int32_t h[kHeaderInts] = {status, (int32_t)N, (int32_t)We, maxle, h4, h5, total, a.T};
+        for (int i = 0; i < kHeaderInts; ++i)
+            a.header[i] = h[i];
+    }
+}
 
 __global__ __launch_bounds__(kPT) void plan_kernel(PlanArgs a)
 {
@@ -102,81 +191,163 @@ __global__ __launch_bounds__(kPT) void plan_kernel(PlanArgs a)
         return;
     }
 
-    // 2d) dynamic: segments per (b, g) and their prefix
-    const int64_t N = (int64_t)total * a.Hkv;
-    const int64_t We = N < a.W ? N : a.W;
-    const int cB = (nbg + kPT - 1) / kPT;
-    const int g0 = min(nbg, tid * cB), g1 = min(nbg, g0 + cB);
-    int segs = 0;
-    for (int bg = g0; bg < g1; ++bg) {
-        const int b = bg / a.Hkv, g = bg - b * a.Hkv;
-        const int64_t nb = tp[b + 1] - tp[b];
-        if (nb == 0) {
-            a.first_wg[bg] = -1;
-        } else {
-            const int64_t u0 = (int64_t)tp[b] * a.Hkv + g * nb;
-            const int64_t w0 = div_floor((u0 + 1) * We - 1, N);
-            const int64_t w1 = div_floor((u0 + nb) * We - 1, N);
-            a.first_wg[bg] = (int32_t)w0;
-            segs += (int)(w1 - w0 + 1);
-        }
-    }
-    int nseg;
-    run = block_excl_scan<kPT>(segs, scan_lds, &nseg);
-    for (int bg = g0; bg < g1; ++bg) {
-        const int b = bg / a.Hkv, g = bg - b * a.Hkv;
-        const int64_t nb = tp[b + 1] - tp[b];
-        if (nb) {
-            const int64_t u0 = (int64_t)tp[b] * a.Hkv + g * nb;
-            run += (int)(div_floor((u0 + nb) * We - 1, N) - div_floor((u0 + 1) * We - 1, N) + 1);
-        }
-        a.seg_prefix[bg + 1] = run;
-    }
-    if (tid == 0)
-        a.seg_prefix[0] = 0;
+    plan_partition(a, tp, a.B, total, status, maxle, 0, 0, scan_lds);
+}
 
-    // 3) workgroup ranges and the request of each range's first unit
-    const int cC = (a.W + 1 + kPT - 1) / kPT;
-    const int w0 = min(a.W + 1, tid * cC), w1 = min(a.W + 1, w0 + cC);
-    int sb = 0;
-    if (w0 < w1 && We > 0) {
-        // largest b in [0, B) with Hkv * tp[b] <= begin(w0)
-        const int64_t begin = w0 <= We ? div_floor((int64_t)w0 * N, We) : N;
-        int lo = 0, hi = a.B - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if ((int64_t)tp[mid] * a.Hkv <= begin)
-                lo = mid;
-            else
-                hi = mid - 1;
-        }
-        sb = lo;
+
+// Group of request b (mode 2): its leader, member count m and the group's
+// shared tokens Ls (0 when m < 2). rs is the start of b's run.
+__device__ __forceinline__ void group_of(const PlanArgs &a, int R, int b, int rs, int &leader, int &m, int &Ls)
+{
+    leader = rs + (b - rs) / R * R;
+    m = 1;
+    Ls = INT32_MAX;
+    while (m < R && leader + m < a.B) {
+        const int sh = a.share[leader + m];
+        if (sh == 0)
+            break;
+        Ls = min(Ls, sh);
+        ++m;
     }
-    for (int w = w0; w < w1; ++w) {
-        const int64_t begin = (w <= We && We > 0) ? div_floor((int64_t)w * N, We) : N;
-        a.wg_begin[w] = (int32_t)begin;
-        if (w < a.W) {
-            if (w < We) {
-                while (sb + 1 < a.B && (int64_t)tp[sb + 1] * a.Hkv <= begin)
-                    ++sb;
-                a.wg_start_b[w] = sb;
-            } else {
-                a.wg_start_b[w] = a.B;
+    if (m < 2)
+        Ls = 0;
+}
+
+// Mode 2: prefix-shared pages. Intermediate arrays live in the workspace; all
+// threads are in one workgroup, so barriers order them.
+__global__ __launch_bounds__(kPT) void plan_shared_kernel(PlanArgs a)
+{
+    __shared__ int scan_lds[kPW];
+    __shared__ int red_lds[2 * kPW];
+    const int tid = threadIdx.x;
+    const int R = shared_group(a.G);
+    const int64_t limit = (int64_t)a.pt_stride * a.P;
+    const int cA = (a.B + kPT - 1) / kPT;
+    const int b0 = min(a.B, tid * cA), b1 = min(a.B, b0 + cA);
+
+    // 1) validated lengths
+    int mx = 0, st = 0;
+    for (int b = b0; b < b1; ++b) {
+        int L = a.lengths[b];
+        if (L < 0 || (int64_t)L > limit) {
+            st = 1;
+            L = 0;
+        }
+        a.len_req[b] = L;
+        mx = max(mx, L);
+    }
+    int maxle, status;
+    block_max_or<kPT>(mx, st, red_lds, &maxle, &status);   // its barriers publish len_req
+
+    // 2) tokens shared with the previous request: leading page slots with the
+    //    same valid id, 16 slots per step (independent loads), capped by both
+    //    lengths, whole tiles
+    for (int b = b0; b < b1; ++b) {
+        int sh = 0;
+        if (b > 0) {
+            const int La = a.len_req[b], Lp = a.len_req[b - 1];
+            const int n = min((La + a.P - 1) / a.P, (Lp + a.P - 1) / a.P);
+            const int32_t *ra = a.page_table + (size_t)b * a.pt_stride;
+            const int32_t *rp = ra - a.pt_stride;
+            int c = 0;
+            for (;;) {
+                uint32_t eq = 0;
+#pragma unroll
+                for (int k = 0; k < 16; ++k) {
+                    const int j = c + k;
+                    if (j < n) {
+                        const int x = ra[j], y = rp[j];
+                        eq |= (uint32_t)(x == y && x >= 0 && x < a.num_pages) << k;
+                    }
+                }
+                const int run16 = __builtin_ctz(~eq);   // leading equal slots of this step (<= 16)
+                c += min(run16, n - c);
+                if (run16 < 16 || c >= n)
+                    break;
             }
+            const int64_t t = min((int64_t)c * a.P, (int64_t)min(La, Lp));
+            sh = (int)(t / a.T * a.T);
+        }
+        a.share[b] = sh;
+    }
+    __syncthreads();
+
+    // 3) runs (start at b = 0 and wherever share = 0), groups of R, and the
+    //    item and tile counts of each thread's requests
+    int last_start = -1;
+    for (int b = b0; b < b1; ++b)
+        if (b == 0 || a.share[b] == 0)
+            last_start = b;
+    const int carry = block_excl_max_scan<kPT>(last_start, -1, scan_lds);
+    int nitems = 0, ntiles = 0;
+    {
+        int rs = carry;
+        for (int b = b0; b < b1; ++b) {
+            if (b == 0 || a.share[b] == 0)
+                rs = b;
+            int leader, m, Ls;
+            group_of(a, R, b, rs, leader, m, Ls);
+            if (b == leader && m >= 2) {
+                ++nitems;
+                ntiles += (Ls + a.T - 1) / a.T;
+            }
+            ++nitems;
+            ntiles += (a.len_req[b] - Ls + a.T - 1) / a.T;
         }
     }
-    if (tid == 0) {
-        const int32_t h[kHeaderInts] = {status, (int32_t)N, (int32_t)We, maxle, 0, 0, total, a.T};
-        for (int i = 0; i < kHeaderInts; ++i)
-            a.header[i] = h[i];
+    int n_items, total;
+    const int ibase = block_excl_scan<kPT>(nitems, scan_lds, &n_items);
+    const int tbase = block_excl_scan<kPT>(ntiles, scan_lds, &total);
+
+    // 4) items, in request order
+    {
+        int i = ibase, t = tbase, rs = carry;
+        for (int b = b0; b < b1; ++b) {
+            if (b == 0 || a.share[b] == 0)
+                rs = b;
+            int leader, m, Ls;
+            group_of(a, R, b, rs, leader, m, Ls);
+            if (b == leader && m >= 2) {
+                a.item_req[i] = b;
+                a.item_start[i] = 0;
+                a.len_eff[i] = Ls;
+                a.item_m[i] = m;
+                a.item_solo[i] = 0;
+                t += (Ls + a.T - 1) / a.T;
+                a.tiles_prefix[i + 1] = t;
+                ++i;
+            }
+            const int Lb = a.len_req[b];
+            a.item_req[i] = b;
+            a.item_start[i] = Ls;
+            a.len_eff[i] = Lb - Ls;
+            a.item_m[i] = 1;
+            a.item_solo[i] = m >= 2 ? 0 : 1;
+            t += (Lb - Ls + a.T - 1) / a.T;
+            a.tiles_prefix[i + 1] = t;
+            a.req_own[b] = i;
+            a.req_member[b] = m >= 2 ? b - leader : 0;
+            // the group's shared item precedes the own items of leader..b
+            a.req_shared[b] = m >= 2 ? i - 1 - (b - leader) : -1;
+            ++i;
+        }
+        if (tid == 0)
+            a.tiles_prefix[0] = 0;
     }
+    __syncthreads();
+
+    // 5) the dynamic partition over items
+    plan_partition(a, a.tiles_prefix, n_items, total, status, maxle, n_items, R, scan_lds);
 }
 
 }  // namespace
 
 hipError_t launch_plan(const PlanArgs &a, hipStream_t st)
 {
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPT), 0, st, a);
+    if (a.mode == MODE_SHARED)
+        hipLaunchKernelGGL(plan_shared_kernel, dim3(1), dim3(kPT), 0, st, a);
+    else
+        hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPT), 0, st, a);
     return hipGetLastError();
 }
 

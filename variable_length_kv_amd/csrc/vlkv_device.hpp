@@ -60,6 +60,35 @@ __device__ __forceinline__ int block_excl_scan(int v, int *lds, int *total)
     return before + incl - v;
 }
 
+// Exclusive running maximum of one int per thread over a workgroup of NT
+// threads (in thread order); `lo` is the identity (returned to thread 0).
+// `lds` holds NT/64 ints. Every thread of the workgroup must call it.
+template <int NT>
+__device__ __forceinline__ int block_excl_max_scan(int v, int lo, int *lds)
+{
+    constexpr int NW = NT / 64;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off, 64);
+        if (lane >= off)
+            incl = max(incl, y);
+    }
+    int excl = __shfl_up(incl, 1, 64);
+    if (lane == 0)
+        excl = lo;
+    if (lane == 63)
+        lds[wave] = incl;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NW; ++i)
+        if (i < wave)
+            excl = max(excl, lds[i]);
+    __syncthreads();  // lds is reused by the next call
+    return excl;
+}
+
 // Max and OR of one int per thread over a workgroup of NT threads; `lds` holds
 // 2*NT/64 ints.
 template <int NT>

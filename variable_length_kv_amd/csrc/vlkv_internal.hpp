@@ -17,15 +17,27 @@ constexpr int kMaxGroup = 16;      // query heads per kv head (one MFMA column b
 constexpr int kMaxBatch = 8192;    // planner keeps the tile prefix in LDS
 constexpr int kHeaderInts = 8;
 
-// header fields
+// header fields (mode 2: H_CHUNK holds the number of items, H_SPLITS the
+// requests per shared pass R)
 enum : int { H_STATUS = 0, H_UNITS = 1, H_WEFF = 2, H_MAXLEN = 3, H_CHUNK = 4, H_SPLITS = 5,
              H_TILES = 6, H_TILE = 7 };
+enum : int { H_ITEMS = 4, H_GROUP = 5 };
 
-// Byte offsets of the workspace regions (all 256-B aligned).
+// plan modes (the public ATTN_DYNAMIC / ATTN_STATIC / ATTN_SHARED)
+enum : int { MODE_DYNAMIC = 0, MODE_STATIC = 1, MODE_SHARED = 2 };
+
+// Requests per shared pass: one MFMA column block holds kMaxGroup query rows.
+__host__ __device__ constexpr int shared_group(int G) { return G >= kMaxGroup ? 1 : kMaxGroup / G; }
+
+// Byte offsets of the workspace regions (all 256-B aligned). In mode 2 the
+// plan is over items (at most 2B): len_eff, tiles_prefix, seg_prefix, first_wg
+// and wg_start_b are indexed by item, and the item_* / req_* regions exist.
 struct WsLayout {
     size_t header, len_eff, tiles_prefix, seg_prefix, first_wg, wg_begin, wg_start_b;
+    size_t item_req, item_start, item_m, item_solo, req_shared, req_member, req_own, share, len_req;
     size_t counters, part_lse, part_o, total;
-    int64_t max_slots;
+    int64_t max_slots, max_items;
+    int slot_rows;   // query rows per partial slot
 };
 
 // Where a decode workgroup's sequence of segments comes from.
@@ -34,6 +46,7 @@ enum PlanSrc : int {
     SRC_STATIC = 1,         // plan arrays written by attn_plan (static mode)
     SRC_FUSED_DYNAMIC = 2,  // single launch: each workgroup derives its range from the lengths
     SRC_FUSED_STATIC = 3,   // single launch, static split-K
+    SRC_SHARED = 4,         // plan arrays written by attn_plan (mode 2: items, prefix-shared pages)
 };
 
 struct Shape {
@@ -44,8 +57,11 @@ WsLayout ws_layout(const Shape &s);
 
 struct PlanArgs {
     const int32_t *lengths;
+    const int32_t *page_table;   // mode 2 only
     int32_t *header, *len_eff, *tiles_prefix, *seg_prefix, *first_wg, *wg_begin, *wg_start_b;
-    int B, Hkv, P, pt_stride, T, W, mode, S;
+    // mode 2 only
+    int32_t *item_req, *item_start, *item_m, *item_solo, *req_shared, *req_member, *req_own, *share, *len_req;
+    int B, Hkv, G, P, pt_stride, num_pages, T, W, mode, S;
 };
 
 struct DecodeArgs {
@@ -58,19 +74,22 @@ struct DecodeArgs {
     const int32_t *page_table;
     int32_t *header;
     const int32_t *len_eff, *tiles_prefix, *seg_prefix, *first_wg, *wg_begin, *wg_start_b;
+    const int32_t *item_req, *item_start, *item_m, *item_solo;   // SRC_SHARED only
     float *part_o, *part_lse;
     uint16_t *out;             // [B][Hq][D] bf16 bits
     float *lse;                // [B][Hq] or null
     int B, Hq, Hkv, G, P, num_pages, pt_stride, blocks_per_tile, S, T, W;
+    int slot_rows;             // query rows per partial slot
     float scale_log2;          // sm_scale * log2(e)
 };
 
 struct CombineArgs {
     const int32_t *header, *seg_prefix;
+    const int32_t *req_shared, *req_member, *req_own, *item_solo;   // mode 2 only
     const float *part_o, *part_lse;
     uint16_t *out;
     float *lse;
-    int B, Hq, Hkv, G, mode, S;
+    int B, Hq, Hkv, G, mode, S, slot_rows;
 };
 
 struct AppendArgs {

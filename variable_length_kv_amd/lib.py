@@ -19,12 +19,12 @@ LIB_PATH = os.path.join(_HERE, "libvlkv_attn.so")
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
 ATTN_KV_BF16, ATTN_KV_FP8_E4M3 = 0, 1
-ATTN_DYNAMIC, ATTN_STATIC = 0, 1
+ATTN_DYNAMIC, ATTN_STATIC, ATTN_SHARED = 0, 1, 2
 ATTN_STATUS_BAD_LENGTH, ATTN_STATUS_BAD_PAGE = 1, 2
 
 EXPORTED = ("attn_check_shape", "attn_workspace_bytes", "attn_static_splits", "attn_device_cu_count",
             "attn_plan", "attn_decode", "attn_combine", "attn_get_status", "attn_read_plan",
-            "attn_workspace_init", "attn_step", "attn_append_kv", "attn_last_error")
+            "attn_workspace_init", "attn_step", "attn_append_kv", "attn_read_plan_items", "attn_last_error")
 
 
 class AttnError(RuntimeError):
@@ -86,6 +86,7 @@ def load():
         "attn_workspace_init": (i32, [SP, P, sz, P]),
         "attn_step": (i32, [SP, P, P, P, P, P, P, P, ctypes.c_float, P, sz, P, P, P]),
         "attn_append_kv": (i32, [SP, P, P, P, P, P, P, P, P, P, sz, P]),
+        "attn_read_plan_items": (i32, [SP, P, P, P, P, P, P, P, P, P]),
         "attn_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sigs.items():
@@ -202,17 +203,34 @@ def attn_get_status(workspace, stream=None) -> int:
 
 
 def attn_read_plan(shape, workspace, stream=None) -> dict:
+    """The plan arrays of the workspace. ATTN_SHARED: over items (cut to the
+    header's item count), plus the item description."""
     import numpy as np
     B, Hkv, W = shape.batch, shape.num_kv_heads, shape.num_wgs
+    n = 2 * B if shape.mode == ATTN_SHARED else B
     out = {
-        "header": np.zeros(8, np.int32), "len_eff": np.zeros(B, np.int32),
-        "tiles_prefix": np.zeros(B + 1, np.int32), "seg_prefix": np.zeros(B * Hkv + 1, np.int32),
-        "first_wg": np.zeros(B * Hkv, np.int32), "wg_begin": np.zeros(W + 1, np.int32),
+        "header": np.zeros(8, np.int32), "len_eff": np.zeros(n, np.int32),
+        "tiles_prefix": np.zeros(n + 1, np.int32), "seg_prefix": np.zeros(n * Hkv + 1, np.int32),
+        "first_wg": np.zeros(n * Hkv, np.int32), "wg_begin": np.zeros(W + 1, np.int32),
         "wg_start_b": np.zeros(W, np.int32),
     }
     keys = ("header", "len_eff", "tiles_prefix", "seg_prefix", "first_wg", "wg_begin", "wg_start_b")
     _check(load().attn_read_plan(_shape(shape), _ptr(workspace),
                                  *[ctypes.c_void_p(out[k].ctypes.data) for k in keys], _stream(stream)))
+    if shape.mode != ATTN_SHARED:
+        return out
+    items = {k: np.zeros(n, np.int32) for k in ("item_req", "item_start", "item_m", "item_solo")}
+    items.update({k: np.zeros(B, np.int32) for k in ("req_shared", "req_member", "req_own")})
+    ikeys = ("item_req", "item_start", "item_m", "item_solo", "req_shared", "req_member", "req_own")
+    _check(load().attn_read_plan_items(_shape(shape), _ptr(workspace),
+                                       *[ctypes.c_void_p(items[k].ctypes.data) for k in ikeys], _stream(stream)))
+    I = int(out["header"][4])
+    out.update(items)
+    for k in ("len_eff", "item_req", "item_start", "item_m", "item_solo"):
+        out[k] = out[k][:I]
+    out["tiles_prefix"] = out["tiles_prefix"][:I + 1]
+    out["seg_prefix"] = out["seg_prefix"][:I * Hkv + 1]
+    out["first_wg"] = out["first_wg"][:I * Hkv]
     return out
 
 

@@ -188,13 +188,17 @@ def _quantize_owned(cache_f: torch.Tensor, scale, lengths, page_table, P):
 
 
 def make_case(name, lengths, *, Hq=8, Hkv=1, P=16, D=HEAD_DIM, kv_dtype="bf16",
-              seed=0, pt_stride=None, extra_pages=0, sm_scale=None) -> Case:
-    """Build a decode step with the given lengths; all randomness from ``seed``."""
+              seed=0, pt_stride=None, extra_pages=0, sm_scale=None, page_table=None, num_pages=None) -> Case:
+    """Build a decode step with the given lengths; all randomness from ``seed``.
+    A given ``page_table`` / ``num_pages`` replaces the random placement."""
     lengths = np.asarray(lengths, np.int32)
     B = len(lengths)
     rng_pages = np.random.default_rng(3 * seed + 1)
     data_seed = 3 * seed + 2
-    pt, num_pages = make_page_table(lengths, P, rng_pages, pt_stride, extra_pages)
+    if page_table is None:
+        pt, num_pages = make_page_table(lengths, P, rng_pages, pt_stride, extra_pages)
+    else:
+        pt, num_pages = np.ascontiguousarray(page_table, np.int32), int(num_pages)
     q = to_bf16(normal_f32(data_seed, (TAG_Q,), B * Hq * D), (B, Hq, D))
     k = _fill_cache_bf16(data_seed, (TAG_K,), num_pages, Hkv, P, D)
     v = _fill_cache_bf16(data_seed, (TAG_V,), num_pages, Hkv, P, D)
@@ -210,6 +214,50 @@ def make_case(name, lengths, *, Hq=8, Hkv=1, P=16, D=HEAD_DIM, kv_dtype="bf16",
         sm_scale = 1.0 / math.sqrt(D)
     return Case(name, B, Hq, Hkv, D, P, lengths, pt, num_pages, kv_dtype, q, k, v, ks, vs,
                 float(sm_scale), {"seed": seed})
+
+
+def shared_page_table(lengths, groups, P, seed):
+    """Page table with prefix caching: ``groups`` lists (first, count,
+    prefix_pages); requests first+1 .. first+count-1 read request first's
+    pages in their first prefix_pages slots, every other slot gets a page of
+    its own. Physical placement is a seeded random permutation. Returns
+    (page_table, num_pages)."""
+    lengths = np.asarray(lengths, np.int64)
+    B = len(lengths)
+    n = (lengths + P - 1) // P
+    alias = {}   # (b, slot) -> (leader, slot)
+    for first, count, npg in groups:
+        for b in range(first + 1, first + count):
+            for j in range(min(int(npg), int(n[b]), int(n[first]))):
+                alias[(b, j)] = (first, j)
+    own = [(b, j) for b in range(B) for j in range(int(n[b])) if (b, j) not in alias]
+    perm = np.random.default_rng(seed).permutation(len(own)).astype(np.int32)
+    pt = np.full((B, max(1, int(n.max()) if B else 1)), -1, np.int32)
+    for (b, j), pid in zip(own, perm):
+        pt[b, j] = pid
+    for (b, j), (f, jj) in alias.items():
+        pt[b, j] = pt[f, jj]
+    return pt, max(1, len(own))
+
+
+def make_shared_case(name, lengths, groups, *, Hq=8, Hkv=1, P=16, kv_dtype="bf16", seed=0) -> Case:
+    """A decode step whose requests share prefix pages (see shared_page_table)."""
+    pt, num_pages = shared_page_table(lengths, groups, P, 3 * seed + 1)
+    c = make_case(name, lengths, Hq=Hq, Hkv=Hkv, P=P, kv_dtype=kv_dtype, seed=seed, page_table=pt,
+                  num_pages=num_pages)
+    c.meta["groups"] = [tuple(int(x) for x in g) for g in groups]
+    return c
+
+
+def shared_prefix_lengths(n_groups, group_size, prefix_tokens, suffix_lo, suffix_hi, P, seed=0):
+    """Agentic batch: n_groups groups of group_size requests that share a
+    prefix_tokens-long prompt (its whole pages are shared), each with its own
+    suffix of U[suffix_lo, suffix_hi] tokens. Returns (lengths, groups) for
+    make_shared_case."""
+    rng = np.random.default_rng(3 * seed)
+    suffix = rng.integers(suffix_lo, suffix_hi, n_groups * group_size, endpoint=True)
+    lengths = (prefix_tokens + suffix).astype(np.int32)
+    return lengths, [(g * group_size, group_size, prefix_tokens // P) for g in range(n_groups)]
 
 
 # --------------------------------------------------------------------------
