@@ -249,6 +249,43 @@ def batch_leg(cid, torch, L, wl, W_of, flush, static_sweep=False):
     return entry
 
 
+def shared_leg(torch, L, wl, W_of, flush, Hq):
+    """Workload 5: prefix caching. 16 groups of 4 requests share an 8192-token
+    prompt (its 128 pages aliased in their page tables), each request with its
+    own suffix of U[64, 2048] tokens; 8 kv heads, page 64, bf16. The dynamic
+    plan (single launch) reads every request's prefix; the shared plan
+    (ATTN_SHARED, three launches) reads a group's prefix once per 16/G
+    requests. Logical bytes count every request's rows; read bytes count the
+    rows the shared plan's items read."""
+    lengths, groups = wl.shared_prefix_lengths(16, 4, 8192, 64, 2048, 64, seed=0)
+    c = wl.make_shared_case("shared", lengths, groups, Hq=Hq, Hkv=8, P=64, seed=0)
+    W = W_of(c.lengths, c.Hkv)
+    r = Runner(c, torch, L, W)
+    per_tok = 2 * c.Hkv * c.D * c.elem_bytes
+    entry = {"requests": c.B, "q_heads": Hq, "kv_heads": c.Hkv, "requests_per_shared_pass": max(1, 16 // c.G),
+             "logical_gb": round(c.kv_bytes / 1e9, 4), "num_wgs": W}
+    a = r.attention(L.ATTN_DYNAMIC)
+    t_dyn = per_step_flushed(r, a, 30, 5, torch, flush, True)
+    entry["dynamic"] = stats(t_dyn, c.kv_bytes)
+    del a
+    a = r.attention(L.ATTN_SHARED)
+    r.plan(a)
+    p = a.read_plan()
+    read = int(np.asarray(p["len_eff"], np.int64).sum()) * per_tok
+    entry["shared_items"] = int((np.asarray(p["item_m"]) > 1).sum())
+    entry["read_gb"] = round(read / 1e9, 4)
+    t_sh = per_step_flushed(r, a, 30, 5, torch, flush, True)
+    med = float(np.median(t_sh))
+    entry["shared"] = {"us_median": us(med), "us_p10": us(np.percentile(t_sh, 10)),
+                       "us_p90": us(np.percentile(t_sh, 90)),
+                       "logical_gbs": round(c.kv_bytes / (med * 1e-3) / 1e9, 1),
+                       "pct_hbm_on_read_bytes": round(100 * read / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+    entry["speedup_vs_dynamic"] = round(entry["dynamic"]["us_median"] / us(med), 3)
+    del a, r
+    torch.cuda.empty_cache()
+    return entry
+
+
 def trace_leg(torch, L, W_of, flush, steps=256):
     """Workload 4: the continuous-batching trace with an fp8 cache. Each step is
     timed alone after a cache flush: the single-launch step (its plan is built
@@ -479,6 +516,10 @@ def main():
         log(f"bench: long_tail: {json.dumps(extra['long_tail'])}")
         extra["trace_fp8"] = trace_leg(torch, L, W_of, flush, args.trace_steps)
         log(f"bench: trace_fp8: {json.dumps(extra['trace_fp8'])}")
+        for hq in (64, 32):
+            key = f"shared_prefix_hq{hq}"
+            extra[key] = shared_leg(torch, L, wl, W_of, flush, hq)
+            log(f"bench: {key}: {json.dumps(extra[key])}")
         del flush
         torch.cuda.empty_cache()
         result["extra"] = extra

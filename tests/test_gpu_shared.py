@@ -159,3 +159,20 @@ def test_run_to_run_determinism():
     a = run(c, t=t, W=41, mode=L.ATTN_SHARED)
     b = run(c, t=t, W=41, mode=L.ATTN_SHARED)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_bench_scale_sampled():
+    """The benchmark's prefix-caching batch at full size (64 requests, 8192-token
+    shared prompts, 8 kv heads, page 64): sampled requests against the CPU
+    reference, in the launch configuration the benchmark times."""
+    lengths, groups = wl.shared_prefix_lengths(16, 4, 8192, 64, 2048, 64, seed=0)
+    for hq in (64, 32):
+        c = wl.make_shared_case("shared", lengths, groups, Hq=hq, Hkv=8, P=64, seed=0)
+        W = L.suggest_num_wgs(L.attn_device_cu_count(0), c.lengths, c.Hkv)
+        out, lse, att = run(c, mode=L.ATTN_SHARED, W=W, fused=True)
+        p = att.read_plan()
+        R = max(1, 16 // c.G)
+        assert (np.asarray(p["item_m"]) > 1).sum() == 16 * -(-4 // R)   # groups of 4 cut into passes of R
+        ids = [0, 1, 2, 3, 17, 30, 45, 63]
+        check_against_oracle(c, out, lse, req_ids=ids, what=f"hq={hq}")
+        assert att.status() == 0

@@ -29,7 +29,8 @@
 // The work is O(B*Hkv + W) and latency-bound: each thread owns a contiguous
 // chunk of every array, so a prefix sum is one serial pass per thread, one
 // wave scan and one exchange of 4 wave totals through LDS. Mode 2 adds the
-// page-table comparison of adjacent requests, 16 slots per dependent step.
+// page-table comparison of adjacent requests: 256 slots per coalesced wave
+// step, 8 requests in flight in each of 16 waves.
 #include "vlkv_device.hpp"
 #include "vlkv_internal.hpp"
 
@@ -38,10 +39,13 @@ namespace {
 
 constexpr int kPT = 256;  // planner threads
 constexpr int kPW = kPT / 64;
+constexpr int kST = 1024; // threads of the prefix-shared planner: more waves keep more
+constexpr int kSW = kST / 64;   // page-table loads in flight (each wave holds at most 63)
 
 // The dynamic partition over n "items" (requests in modes 0, items in mode
 // 2) whose tiles prefix is tp[0..n]: segments of each (item, kv head) pair and
 // their prefix, each workgroup's range and first item, and the header.
+template <int NT>
 __device__ void plan_partition(const PlanArgs &a, const int32_t *tp, int n, int total, int status, int maxle,
                                int h4, int h5, int *scan_lds)
 {
@@ -51,7 +55,7 @@ __device__ void plan_partition(const PlanArgs &a, const int32_t *tp, int n, int 
     const int nbg = n * a.Hkv;
     const int64_t N = (int64_t)total * a.Hkv;
     const int64_t We = N < a.W ? N : a.W;
-    const int cB = (nbg + kPT - 1) / kPT;
+    const int cB = (nbg + NT - 1) / NT;
     const int g0 = min(nbg, tid * cB), g1 = min(nbg, g0 + cB);
     int segs = 0;
     for (int bg = g0; bg < g1; ++bg) {
@@ -68,7 +72,7 @@ __device__ void plan_partition(const PlanArgs &a, const int32_t *tp, int n, int 
         }
     }
     int nseg;
-    run = block_excl_scan<kPT>(segs, scan_lds, &nseg);
+    run = block_excl_scan<NT>(segs, scan_lds, &nseg);
     for (int bg = g0; bg < g1; ++bg) {
         const int b = bg / a.Hkv, g = bg - b * a.Hkv;
         const int64_t nb = tp[b + 1] - tp[b];
@@ -82,7 +86,7 @@ __device__ void plan_partition(const PlanArgs &a, const int32_t *tp, int n, int 
         a.seg_prefix[0] = 0;
 
     // 3) workgroup ranges and the request of each range's first unit
-    const int cC = (a.W + 1 + kPT - 1) / kPT;
+    const int cC = (a.W + 1 + NT - 1) / NT;
     const int w0 = min(a.W + 1, tid * cC), w1 = min(a.W + 1, w0 + cC);
     int sb = 0;
     if (w0 < w1 && We > 0) {
@@ -191,7 +195,7 @@ __global__ __launch_bounds__(kPT) void plan_kernel(PlanArgs a)
         return;
     }
 
-    plan_partition(a, tp, a.B, total, status, maxle, 0, 0, scan_lds);
+    plan_partition<kPT>(a, tp, a.B, total, status, maxle, 0, 0, scan_lds);
 }
 
 
@@ -215,17 +219,98 @@ __device__ __forceinline__ void group_of(const PlanArgs &a, int R, int b, int rs
 
 // Mode 2: prefix-shared pages. Intermediate arrays live in the workspace; all
 // threads are in one workgroup, so barriers order them.
-__global__ __launch_bounds__(kPT) void plan_shared_kernel(PlanArgs a)
+__global__ __launch_bounds__(kST) void plan_shared_kernel(PlanArgs a)
 {
-    __shared__ int scan_lds[kPW];
-    __shared__ int red_lds[2 * kPW];
+    __shared__ int32_t tp_lds[kMaxBatch + 1];   // item tiles prefix, when at most kMaxBatch items
+    __shared__ int scan_lds[kSW];
+    __shared__ int red_lds[2 * kSW];
     const int tid = threadIdx.x;
     const int R = shared_group(a.G);
     const int64_t limit = (int64_t)a.pt_stride * a.P;
-    const int cA = (a.B + kPT - 1) / kPT;
+    const int cA = (a.B + kST - 1) / kST;
     const int b0 = min(a.B, tid * cA), b1 = min(a.B, b0 + cA);
 
-    // 1) validated lengths
+    // 1) tokens shared with the previous request: leading page slots with the
+    //    same valid id, capped by both lengths, whole tiles. It reads only the
+    //    inputs, so it goes first. Lane l of a wave
+    //    compares slots 4l..4l+3 (256 consecutive slots per step, coalesced);
+    //    a ballot over the lanes whose 4 slots all agree finds the first
+    //    mismatch. Each of the 16 waves takes kNB requests at a time
+    //    (b = wave + 16 k), so all their loads share one round trip per step;
+    //    the round trips, not the bytes, are what this phase costs (a wave
+    //    holds at most 63 loads in flight, hence the 16 waves).
+    {
+        constexpr int kNB = 8, kSub = 4, kSpan = 64 * kSub;
+        const int wave = tid >> 6, lane = tid & 63;
+        for (int base = wave; base < a.B; base += kSW * kNB) {
+            int c[kNB], n[kNB], lmin[kNB];
+            bool done[kNB];
+#pragma unroll
+            for (int k = 0; k < kNB; ++k) {
+                // branch-free, in-bounds loads (all of them in one round trip)
+                const int b = base + kSW * k;
+                const int ia = max(min(b, a.B - 1), 0), ip = max(ia - 1, 0);
+                int la = a.lengths[ia], lp = a.lengths[ip];
+                la = (la < 0 || (int64_t)la > limit) ? 0 : la;   // validated as in step 1
+                lp = (lp < 0 || (int64_t)lp > limit) ? 0 : lp;
+                lmin[k] = min(la, lp);
+                c[k] = 0;
+                n[k] = (b > 0 && b < a.B) ? (lmin[k] + a.P - 1) / a.P : 0;
+                done[k] = n[k] == 0;
+            }
+            for (;;) {
+                int x[kNB][kSub], y[kNB][kSub];
+#pragma unroll
+                for (int k = 0; k < kNB; ++k) {
+                    const int32_t *ra = a.page_table + (size_t)(base + kSW * k) * a.pt_stride;
+#pragma unroll
+                    for (int i = 0; i < kSub; ++i) {
+                        x[k][i] = -1;
+                        y[k][i] = -2;
+                        const int j = c[k] + kSub * lane + i;
+                        if (!done[k] && j < n[k]) {
+                            x[k][i] = ra[j];
+                            y[k][i] = ra[j - a.pt_stride];
+                        }
+                    }
+                }
+                bool any = false;
+#pragma unroll
+                for (int k = 0; k < kNB; ++k) {
+                    if (done[k])
+                        continue;
+                    int m = 0;   // this lane's slots that agree (slots past n do not)
+#pragma unroll
+                    for (int i = 0; i < kSub; ++i)
+                        m |= (x[k][i] == y[k][i] && x[k][i] >= 0 && x[k][i] < a.num_pages) << i;
+                    const uint64_t full = __builtin_amdgcn_ballot_w64(m == (1 << kSub) - 1);
+                    int run = kSpan;
+                    if (full != ~0ull) {
+                        const int fl = __builtin_ctzll(~full);   // first lane with a mismatch
+                        const int mf = __builtin_amdgcn_readlane(m, fl);
+                        run = kSub * fl + __builtin_ctz(~mf);
+                    }
+                    c[k] += run;
+                    done[k] = run < kSpan || c[k] >= n[k];
+                    any |= !done[k];
+                }
+                if (!any)
+                    break;
+            }
+            if (lane == 0) {
+#pragma unroll
+                for (int k = 0; k < kNB; ++k) {
+                    const int b = base + kSW * k;
+                    if (b < a.B) {
+                        const int64_t t = b > 0 ? min((int64_t)c[k] * a.P, (int64_t)lmin[k]) : 0;
+                        a.share[b] = (int)(t / a.T * a.T);
+                    }
+                }
+            }
+        }
+    }
+
+    // 2) validated lengths
     int mx = 0, st = 0;
     for (int b = b0; b < b1; ++b) {
         int L = a.lengths[b];
@@ -237,40 +322,7 @@ __global__ __launch_bounds__(kPT) void plan_shared_kernel(PlanArgs a)
         mx = max(mx, L);
     }
     int maxle, status;
-    block_max_or<kPT>(mx, st, red_lds, &maxle, &status);   // its barriers publish len_req
-
-    // 2) tokens shared with the previous request: leading page slots with the
-    //    same valid id, 16 slots per step (independent loads), capped by both
-    //    lengths, whole tiles
-    for (int b = b0; b < b1; ++b) {
-        int sh = 0;
-        if (b > 0) {
-            const int La = a.len_req[b], Lp = a.len_req[b - 1];
-            const int n = min((La + a.P - 1) / a.P, (Lp + a.P - 1) / a.P);
-            const int32_t *ra = a.page_table + (size_t)b * a.pt_stride;
-            const int32_t *rp = ra - a.pt_stride;
-            int c = 0;
-            for (;;) {
-                uint32_t eq = 0;
-#pragma unroll
-                for (int k = 0; k < 16; ++k) {
-                    const int j = c + k;
-                    if (j < n) {
-                        const int x = ra[j], y = rp[j];
-                        eq |= (uint32_t)(x == y && x >= 0 && x < a.num_pages) << k;
-                    }
-                }
-                const int run16 = __builtin_ctz(~eq);   // leading equal slots of this step (<= 16)
-                c += min(run16, n - c);
-                if (run16 < 16 || c >= n)
-                    break;
-            }
-            const int64_t t = min((int64_t)c * a.P, (int64_t)min(La, Lp));
-            sh = (int)(t / a.T * a.T);
-        }
-        a.share[b] = sh;
-    }
-    __syncthreads();
+    block_max_or<kST>(mx, st, red_lds, &maxle, &status);   // its barriers publish len_req and share
 
     // 3) runs (start at b = 0 and wherever share = 0), groups of R, and the
     //    item and tile counts of each thread's requests
@@ -278,7 +330,7 @@ __global__ __launch_bounds__(kPT) void plan_shared_kernel(PlanArgs a)
     for (int b = b0; b < b1; ++b)
         if (b == 0 || a.share[b] == 0)
             last_start = b;
-    const int carry = block_excl_max_scan<kPT>(last_start, -1, scan_lds);
+    const int carry = block_excl_max_scan<kST>(last_start, -1, scan_lds);
     int nitems = 0, ntiles = 0;
     {
         int rs = carry;
@@ -296,8 +348,8 @@ __global__ __launch_bounds__(kPT) void plan_shared_kernel(PlanArgs a)
         }
     }
     int n_items, total;
-    const int ibase = block_excl_scan<kPT>(nitems, scan_lds, &n_items);
-    const int tbase = block_excl_scan<kPT>(ntiles, scan_lds, &total);
+    const int ibase = block_excl_scan<kST>(nitems, scan_lds, &n_items);
+    const int tbase = block_excl_scan<kST>(ntiles, scan_lds, &total);
 
     // 4) items, in request order
     {
@@ -315,6 +367,8 @@ __global__ __launch_bounds__(kPT) void plan_shared_kernel(PlanArgs a)
                 a.item_solo[i] = 0;
                 t += (Ls + a.T - 1) / a.T;
                 a.tiles_prefix[i + 1] = t;
+                if (i + 1 <= kMaxBatch)
+                    tp_lds[i + 1] = t;
                 ++i;
             }
             const int Lb = a.len_req[b];
@@ -325,19 +379,24 @@ __global__ __launch_bounds__(kPT) void plan_shared_kernel(PlanArgs a)
             a.item_solo[i] = m >= 2 ? 0 : 1;
             t += (Lb - Ls + a.T - 1) / a.T;
             a.tiles_prefix[i + 1] = t;
+            if (i + 1 <= kMaxBatch)
+                tp_lds[i + 1] = t;
             a.req_own[b] = i;
             a.req_member[b] = m >= 2 ? b - leader : 0;
             // the group's shared item precedes the own items of leader..b
             a.req_shared[b] = m >= 2 ? i - 1 - (b - leader) : -1;
             ++i;
         }
-        if (tid == 0)
+        if (tid == 0) {
             a.tiles_prefix[0] = 0;
+            tp_lds[0] = 0;
+        }
     }
     __syncthreads();
 
-    // 5) the dynamic partition over items
-    plan_partition(a, a.tiles_prefix, n_items, total, status, maxle, n_items, R, scan_lds);
+    // 5) the dynamic partition over items (tiles prefix from LDS when it fits)
+    plan_partition<kST>(a, n_items <= kMaxBatch ? tp_lds : a.tiles_prefix, n_items, total, status, maxle, n_items, R,
+                   scan_lds);
 }
 
 }  // namespace
@@ -345,7 +404,7 @@ __global__ __launch_bounds__(kPT) void plan_shared_kernel(PlanArgs a)
 hipError_t launch_plan(const PlanArgs &a, hipStream_t st)
 {
     if (a.mode == MODE_SHARED)
-        hipLaunchKernelGGL(plan_shared_kernel, dim3(1), dim3(kPT), 0, st, a);
+        hipLaunchKernelGGL(plan_shared_kernel, dim3(1), dim3(kST), 0, st, a);
     else
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPT), 0, st, a);
     return hipGetLastError();
