@@ -432,6 +432,8 @@ def main():
     ap.add_argument("--wgs-per-cu", type=int, default=0,
                     help="workgroups per CU of the dynamic plan (0: the library's suggestion per workload)")
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
+    ap.add_argument("--extra-legs", default="skewed,long_tail,trace,shared",
+                    help="comma list of the extra workloads to run (skewed, long_tail, trace, shared)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--trace-steps", type=int, default=256)
     ap.add_argument("--traffic-probe", action="store_true",
@@ -509,17 +511,22 @@ def main():
     # ---- extra workloads ------------------------------------------------------
     if not args.no_extra:
         extra = {}
+        legs = set(args.extra_legs.split(","))
         flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
-        extra["skewed"] = batch_leg(2, torch, L, wl, W_of, flush, static_sweep=True)
-        log(f"bench: skewed: {json.dumps(extra['skewed'])}")
-        extra["long_tail"] = batch_leg(3, torch, L, wl, W_of, flush)
-        log(f"bench: long_tail: {json.dumps(extra['long_tail'])}")
-        extra["trace_fp8"] = trace_leg(torch, L, W_of, flush, args.trace_steps)
-        log(f"bench: trace_fp8: {json.dumps(extra['trace_fp8'])}")
-        for hq in (64, 32):
-            key = f"shared_prefix_hq{hq}"
-            extra[key] = shared_leg(torch, L, wl, W_of, flush, hq)
-            log(f"bench: {key}: {json.dumps(extra[key])}")
+        if "skewed" in legs:
+            extra["skewed"] = batch_leg(2, torch, L, wl, W_of, flush, static_sweep=True)
+            log(f"bench: skewed: {json.dumps(extra['skewed'])}")
+        if "long_tail" in legs:
+            extra["long_tail"] = batch_leg(3, torch, L, wl, W_of, flush)
+            log(f"bench: long_tail: {json.dumps(extra['long_tail'])}")
+        if "trace" in legs:
+            extra["trace_fp8"] = trace_leg(torch, L, W_of, flush, args.trace_steps)
+            log(f"bench: trace_fp8: {json.dumps(extra['trace_fp8'])}")
+        if "shared" in legs:
+            for hq in (64, 32):
+                key = f"shared_prefix_hq{hq}"
+                extra[key] = shared_leg(torch, L, wl, W_of, flush, hq)
+                log(f"bench: {key}: {json.dumps(extra[key])}")
         del flush
         torch.cuda.empty_cache()
         result["extra"] = extra
