@@ -190,10 +190,26 @@ def cpu_baseline(case, budget_s=10.0):
         t_total += time.perf_counter() - t0
         passes += 1
     nbytes = case.kv_bytes * passes
+    # one thread, on the first eighth of the requests (a bounded sample of the same workload)
+    ids = list(range(max(1, case.B // 8)))
+    sub_bytes = 2 * case.Hkv * case.D * case.elem_bytes * int(np.asarray(case.lengths)[ids].sum())
+    t0 = time.perf_counter()
+    oracle.decode(case, req_ids=ids, threads=1)
+    t1 = time.perf_counter() - t0
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{passes} whole passes over the headline workload ({case.B} requests, "
                       f"{case.total_tokens} tokens, {case.kv_bytes / 1e6:.1f} MB of KV each) in "
-                      f"{t_total:.1f} s; fp64 C, OpenMP over (request, kv head)"}
+                      f"{t_total:.1f} s; fp64 C, OpenMP over (request, kv head)",
+            "value_1_thread": round(sub_bytes / t1 / 1e9, 4),
+            "sample_1_thread": f"requests 0..{len(ids) - 1} of the same workload ({sub_bytes / 1e6:.1f} MB of KV) "
+                               f"in {t1:.1f} s on one thread",
+            "cpu_model": model}
 
 
 def stats(ts_ms, kv_bytes):
@@ -244,6 +260,18 @@ def batch_leg(cid, torch, L, wl, W_of, flush, static_sweep=False):
         entry["three_launch_speedup_vs_static_default"] = round(
             entry["static_default_three_launch"]["us_median"] / d3, 3)
         entry["three_launch_speedup_vs_best_static"] = round(min(sweep3.values()) / d3, 3)
+    if cid == 2:
+        # the long request last instead of first: static's worse case
+        cl = wl.config_case(2, long_last=True)
+        rl = Runner(cl, torch, L, W)
+        a = rl.attention(L.ATTN_DYNAMIC)
+        t = per_step_flushed(rl, a, 20, 3, torch, flush, True)
+        del a
+        a = rl.attention(L.ATTN_STATIC)
+        ts = per_step_flushed(rl, a, 20, 3, torch, flush, True)
+        del a, rl
+        entry["long_request_last"] = {"dynamic": stats(t, cl.kv_bytes), "static_default": stats(ts, cl.kv_bytes),
+                                      "speedup_vs_static_default": round(float(np.median(ts) / np.median(t)), 3)}
     del r
     torch.cuda.empty_cache()
     return entry
