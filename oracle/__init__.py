@@ -41,6 +41,12 @@ def _load():
         lib.oracle_plan.argtypes = [i32] * 8 + [P] * 8
         lib.oracle_plan_shared.restype = i32
         lib.oracle_plan_shared.argtypes = [i32] * 8 + [P] * 16
+        lib.oracle_bf16_rne.restype = ctypes.c_uint16
+        lib.oracle_bf16_rne.argtypes = [ctypes.c_float]
+        lib.oracle_router_split.restype = None
+        lib.oracle_router_split.argtypes = [P, P, P, ctypes.c_int64]
+        lib.oracle_router_gemm.restype = i32
+        lib.oracle_router_gemm.argtypes = [i32] * 3 + [P] * 6 + [i32]
         lib.oracle_bf16_to_f64.restype = ctypes.c_double
         lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
         lib.oracle_e4m3fn_to_f64.restype = ctypes.c_double
@@ -207,3 +213,39 @@ def plan_shared(lengths, page_table, Hkv, G, P, num_pages, T, W):
     out["seg_prefix"] = out["seg_prefix"][:I * Hkv + 1]
     out["first_wg"] = out["first_wg"][:I * Hkv]
     return out
+
+
+def bf16_rne(value: float) -> int:
+    """fp32 -> bf16 bits by round to nearest, ties to even."""
+    return int(_load().oracle_bf16_rne(ctypes.c_float(value)))
+
+
+def router_split(w):
+    """Split fp32 weights into bf16 (hi, lo) bit arrays: hi = bf16(w),
+    lo = bf16(256 (w - hi)). Returns two uint16 arrays of w's shape."""
+    w32 = np.ascontiguousarray(_np(w, np.float32))
+    hi = np.empty(w32.shape, np.uint16)
+    lo = np.empty(w32.shape, np.uint16)
+    _load().oracle_router_split(_ptr(w32), _ptr(hi), _ptr(lo), w32.size)
+    return hi, lo
+
+
+def router_gemm(x_bits, w, hi=None, lo=None, threads=0):
+    """fp64 y[M][E] = x[M][K] w[E][K]^T, with the exact fp32 weights and with
+    hi + lo/256. x_bits: bf16 bits (uint16 array or bf16 tensor). Returns
+    (y_exact, y_split)."""
+    x = np.ascontiguousarray(_np(x_bits, np.uint16))
+    w32 = np.ascontiguousarray(_np(w, np.float32))
+    if hi is None or lo is None:
+        hi, lo = router_split(w32)
+    M, K = x.shape
+    E = w32.shape[0]
+    if w32.shape != (E, K):
+        raise ValueError("w must be [E][K]")
+    ye = np.zeros((M, E), np.float64)
+    ys = np.zeros((M, E), np.float64)
+    rc = _load().oracle_router_gemm(M, K, E, _ptr(x), _ptr(w32), _ptr(np.ascontiguousarray(hi, np.uint16)),
+                                    _ptr(np.ascontiguousarray(lo, np.uint16)), _ptr(ye), _ptr(ys), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_router_gemm failed with code {rc}")
+    return ye, ys

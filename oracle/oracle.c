@@ -605,3 +605,76 @@ int oracle_append(int32_t B, int32_t Hkv, int32_t D, int32_t P, int32_t num_page
     }
     return status;
 }
+
+/* ------------------------------------------------------------ router GEMM -- */
+/*
+ * Router GEMM with split weights. The source article describes the router
+ * matmul that picks MoE experts as precision-sensitive: each fp32 weight is
+ * split into two bf16 parts, one holding the high part of the weight and one
+ * holding a scaled residual, with a documented scale of 1/256; the kernel runs
+ * two bf16 tensor-core products and combines them [Tencent HPC lands in SGLang,
+ * challenging default inference kernels, sec. "Dynamic Attention and Fused MoE
+ * target different bottlenecks"]. The reading used here:
+ *
+ *   hi = bf16(w),  lo = bf16(256 (w - hi)),  w ~ hi + lo / 256
+ *
+ * with bf16() round-to-nearest-even of the fp32 value (w - hi is exact in fp32:
+ * hi keeps w's 8 leading significant bits). The product of bf16 activations
+ * x[M][K] with the weights w[E][K] (one row per expert) is
+ *
+ *   y[m][e] = sum_k x[m][k] w[e][k]
+ *
+ * oracle_router_gemm returns it twice in fp64: with the exact fp32 weights (the
+ * accuracy target) and with hi + lo/256 (what the split computes before any
+ * accumulation rounding).
+ */
+
+/* fp32 -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN. */
+uint16_t oracle_bf16_rne(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu))
+        return (uint16_t)((u >> 16) | 0x0040u);
+    /* add half an ulp of the kept part (minus one when the kept lsb is 0, so
+       an exact tie stays even), then truncate */
+    const uint32_t lsb = (u >> 16) & 1u;
+    u += 0x7FFFu + lsb;
+    return (uint16_t)(u >> 16);
+}
+
+void oracle_router_split(const float *w, uint16_t *hi, uint16_t *lo, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        const uint16_t h = oracle_bf16_rne(w[i]);
+        const float hf = (float)oracle_bf16_to_f64(h);
+        const float r = (w[i] - hf) * 256.0f;   /* both steps exact for finite w below bf16 overflow */
+        hi[i] = h;
+        lo[i] = oracle_bf16_rne(r);
+    }
+}
+
+int oracle_router_gemm(int32_t M, int32_t K, int32_t E, const uint16_t *x, const float *w, const uint16_t *hi,
+                       const uint16_t *lo, double *y_exact, double *y_split, int32_t threads)
+{
+    if (M < 0 || K < 0 || E < 0 || !x || !w || !hi || !lo || !y_exact || !y_split)
+        return ORACLE_EINVAL;
+#ifdef _OPENMP
+    if (threads <= 0)
+        threads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(threads)
+#endif
+    for (int64_t me = 0; me < (int64_t)M * E; ++me) {
+        const int64_t m = me / E, e = me % E;
+        double a = 0.0, s = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double xv = oracle_bf16_to_f64(x[m * K + k]);
+            a += xv * (double)w[e * K + k];
+            s += xv * (oracle_bf16_to_f64(hi[e * K + k]) + oracle_bf16_to_f64(lo[e * K + k]) / 256.0);
+        }
+        y_exact[me] = a;
+        y_split[me] = s;
+    }
+    (void)threads;
+    return 0;
+}
