@@ -17,7 +17,7 @@ def _declared():
     for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
         src = open(h).read()
         src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-        names |= set(re.findall(r"\b(attn_[a-z_0-9]+)\s*\(", src))
+        names |= set(re.findall(r"\b((?:attn|router)_[a-z_0-9]+)\s*\(", src))
     return names
 
 
@@ -123,3 +123,21 @@ def test_append_rejects_bad_arguments_before_launch():
     odd = ctypes.c_void_p(258)
     assert lib.attn_append_kv(ctypes.byref(s), odd, *args[1:]) == L.ATTN_ERR_INVALID_ARG
     assert b"aligned" in lib.attn_last_error()
+
+
+def test_router_shape_checks_on_the_host():
+    lib = L.load()
+    assert lib.router_workspace_bytes(0, 64, 16) == 0          # M < 1
+    assert lib.router_workspace_bytes(4, 48, 16) == 0          # K not a multiple of 32
+    assert lib.router_workspace_bytes(4, 64, 24) == 0          # E not a multiple of 16
+    assert lib.router_workspace_bytes(8192, 7168, 256) == 0    # enough tiles: no split over K
+    n = lib.router_workspace_bytes(16, 7168, 256)              # few tokens: K split, fp32 partials
+    assert n > 0 and n % (16 * 256 * 4) == 0
+    rc = lib.router_gemm(4, 48, 16, None, None, None, None, None, 0, None)
+    assert rc == L.ATTN_ERR_INVALID_ARG and b"multiple of 32" in lib.attn_last_error()
+    rc = lib.router_gemm(4, 64, 16, None, None, None, None, None, 0, None)
+    assert rc == L.ATTN_ERR_INVALID_ARG and b"non-NULL" in lib.attn_last_error()
+    rc = lib.router_gemm(16, 7168, 256, 16, 16, 16, 16, None, 0, None)   # workspace needed
+    assert rc == L.ATTN_ERR_INVALID_ARG and b"workspace" in lib.attn_last_error()
+    assert lib.router_split_weights(None, None, None, -1, None) == L.ATTN_ERR_INVALID_ARG
+    assert lib.router_split_weights(None, None, None, 0, None) == L.ATTN_OK

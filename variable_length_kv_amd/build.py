@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libvlkv_attn.so")
-SOURCES = ["plan.hip", "decode.hip", "append.hip", "api.hip"]
+SOURCES = ["plan.hip", "decode.hip", "append.hip", "router.hip", "api.hip"]
 ARCH = "gfx950"
 
 

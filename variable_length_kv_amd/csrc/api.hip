@@ -14,8 +14,7 @@ namespace vlkv {
 
 static thread_local std::string g_last_error;
 
-static int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
-static int fail(int code, const char *fmt, ...)
+int fail(int code, const char *fmt, ...)
 {
     char buf[512];
     va_list ap;
@@ -26,7 +25,7 @@ static int fail(int code, const char *fmt, ...)
     return code;
 }
 
-static int ok()
+int ok()
 {
     g_last_error.clear();
     return ATTN_OK;

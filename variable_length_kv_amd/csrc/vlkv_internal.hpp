@@ -102,6 +102,10 @@ struct AppendArgs {
     int B, Hkv, P, num_pages, pt_stride;
 };
 
+// Error reporting of the C ABI (attn_last_error): set the message, return code.
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int ok();
+
 hipError_t launch_plan(const PlanArgs &a, hipStream_t st);
 hipError_t launch_append(const AppendArgs &a, int kv_fp8, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs &a, int src, int kv_fp8, int grid, hipStream_t st);

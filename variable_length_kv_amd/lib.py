@@ -24,7 +24,8 @@ ATTN_STATUS_BAD_LENGTH, ATTN_STATUS_BAD_PAGE = 1, 2
 
 EXPORTED = ("attn_check_shape", "attn_workspace_bytes", "attn_static_splits", "attn_device_cu_count",
             "attn_plan", "attn_decode", "attn_combine", "attn_get_status", "attn_read_plan",
-            "attn_workspace_init", "attn_step", "attn_append_kv", "attn_read_plan_items", "attn_last_error")
+            "attn_workspace_init", "attn_step", "attn_append_kv", "attn_read_plan_items", "attn_last_error",
+            "router_split_weights", "router_workspace_bytes", "router_gemm")
 
 
 class AttnError(RuntimeError):
@@ -87,6 +88,9 @@ def load():
         "attn_step": (i32, [SP, P, P, P, P, P, P, P, ctypes.c_float, P, sz, P, P, P]),
         "attn_append_kv": (i32, [SP, P, P, P, P, P, P, P, P, P, sz, P]),
         "attn_read_plan_items": (i32, [SP, P, P, P, P, P, P, P, P, P]),
+        "router_split_weights": (i32, [P, P, P, ctypes.c_int64, P]),
+        "router_workspace_bytes": (sz, [i32, i32, i32]),
+        "router_gemm": (i32, [i32, i32, i32, P, P, P, P, P, sz, P]),
         "attn_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sigs.items():
@@ -289,3 +293,38 @@ class Attention:
 
     def read_plan(self, stream=None) -> dict:
         return attn_read_plan(self.shape, self.workspace, stream)
+
+
+# ---------------------------------------------------------------- router GEMM --
+
+def router_split_weights(w, w_hi, w_lo, stream=None):
+    """w_hi = bf16(w), w_lo = bf16(256 (w - w_hi)) on the device (tensors: w
+    fp32, w_hi / w_lo bf16 or int16 of w's size)."""
+    if w.numel() != w_hi.numel() or w.numel() != w_lo.numel():
+        raise ValueError("w, w_hi and w_lo must have the same number of elements")
+    _check(load().router_split_weights(_ptr(w), _ptr(w_hi), _ptr(w_lo), ctypes.c_int64(w.numel()),
+                                       _stream(stream)))
+
+
+def router_workspace_bytes(M, K, E) -> int:
+    return int(load().router_workspace_bytes(int(M), int(K), int(E)))
+
+
+class RouterGemm:
+    """y = x w^T with split bf16 weights for one (M, K, E); owns its workspace."""
+
+    def __init__(self, M, K, E, device="cuda"):
+        self.M, self.K, self.E = int(M), int(K), int(E)
+        n = router_workspace_bytes(self.M, self.K, self.E)
+        if n == 0 and load().router_workspace_bytes(self.M, self.K, self.E) == 0:
+            # 0 is also the answer for an invalid shape; router_gemm reports which
+            pass
+        self.workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=device) if n else None
+        self._ws = (_ptr(self.workspace), ctypes.c_size_t(n)) if n else (None, ctypes.c_size_t(0))
+
+    def __call__(self, x, w_hi, w_lo, y, stream=None):
+        if x.shape != (self.M, self.K) or w_hi.shape != (self.E, self.K) or w_lo.shape != (self.E, self.K) \
+                or y.shape != (self.M, self.E):
+            raise ValueError("router_gemm: x [M,K], w_hi/w_lo [E,K], y [M,E]")
+        _check(load().router_gemm(self.M, self.K, self.E, _ptr(x), _ptr(w_hi), _ptr(w_lo), _ptr(y), self._ws[0],
+                                  self._ws[1], _stream(stream)))
