@@ -122,6 +122,23 @@ def bracketed(fn, steps, torch):
     return start.elapsed_time(end) / steps
 
 
+def bracketed_ahead(fn, steps, torch, spin_cycles=4_000_000):
+    """As bracketed, but behind a spin kernel of about a millisecond, so that
+    the host has queued every call before the first one starts: the events
+    then see the GPU's time for short calls, not the host's time to issue
+    them."""
+    fn()
+    start, end = ev(torch), ev(torch)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(spin_cycles)
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
 def timed_three(run, att, steps, warmup, torch):
     """Three-launch steps back to back. Returns (ms per step from events around
     all K steps, per-launch ms [K, 3] from a second pass with HIP events around
@@ -314,6 +331,47 @@ def shared_leg(torch, L, wl, W_of, flush, Hq):
     return entry
 
 
+ROUTER_SHAPES = ((16, 7168, 256), (512, 7168, 256), (8192, 7168, 256), (4096, 4096, 128))
+MFMA_BF16_PEAK_TFS = 2500.0
+
+
+def router_leg(torch, L, reps=30):
+    """Router GEMM (y = x w^T, fp32 weights split into two bf16 parts) at
+    decode, mid and prefill token counts: the split-bf16 MFMA kernel against
+    torch's fp32 product of the same operands and its bf16 product with the
+    weights rounded to bf16. fp32-GEMM flops = 2 M K E; the kernel runs twice
+    that on the matrix cores. Each figure is the mean over `reps` calls queued
+    behind a spin kernel (one warm-up call first)."""
+    d = "cuda:0"
+    out = {}
+    for M, K, E in ROUTER_SHAPES:
+        g = torch.Generator(device=d).manual_seed(M + K + E)
+        x = torch.randn(M, K, generator=g, device=d).to(torch.bfloat16)
+        w = torch.randn(E, K, generator=g, device=d) * 0.02
+        hi = torch.empty(E, K, dtype=torch.bfloat16, device=d)
+        lo = torch.empty_like(hi)
+        L.router_split_weights(w, hi, lo)
+        y = torch.empty(M, E, dtype=torch.float32, device=d)
+        gemm = L.RouterGemm(M, K, E, d)
+        xf = x.float()
+        split_ms = bracketed_ahead(lambda: gemm(x, hi, lo, y), reps, torch)
+        fp32_ms = bracketed_ahead(lambda: torch.matmul(xf, w.t()), reps, torch)
+        hic = hi.contiguous()
+        bf16_ms = bracketed_ahead(lambda: torch.matmul(x, hic.t()), reps, torch)
+        flops = 2.0 * M * K * E
+        key = f"{M}x{K}x{E}"
+        out[key] = {"split_us": us(split_ms), "torch_fp32_us": us(fp32_ms), "torch_bf16_weights_us": us(bf16_ms),
+                    "split_fp32_equiv_tflops": round(flops / (split_ms * 1e-3) / 1e12, 2),
+                    "mfma_tflops": round(2 * flops / (split_ms * 1e-3) / 1e12, 2),
+                    "mfma_pct_of_bf16_peak": round(100 * 2 * flops / (split_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 2),
+                    "weight_gb_s": round(4.0 * E * K / (split_ms * 1e-3) / 1e9, 1),
+                    "speedup_vs_torch_fp32": round(fp32_ms / split_ms, 3),
+                    "k_split_workspace_bytes": L.router_workspace_bytes(M, K, E)}
+        del x, w, hi, lo, y, gemm, xf, hic
+    torch.cuda.empty_cache()
+    return out
+
+
 def trace_leg(torch, L, W_of, flush, steps=256):
     """Workload 4: the continuous-batching trace with an fp8 cache. Each step is
     timed alone after a cache flush: the single-launch step (its plan is built
@@ -460,8 +518,8 @@ def main():
     ap.add_argument("--wgs-per-cu", type=int, default=0,
                     help="workgroups per CU of the dynamic plan (0: the library's suggestion per workload)")
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
-    ap.add_argument("--extra-legs", default="skewed,long_tail,trace,shared",
-                    help="comma list of the extra workloads to run (skewed, long_tail, trace, shared)")
+    ap.add_argument("--extra-legs", default="skewed,long_tail,trace,shared,router",
+                    help="comma list of the extra workloads to run (skewed, long_tail, trace, shared, router)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--trace-steps", type=int, default=256)
     ap.add_argument("--traffic-probe", action="store_true",
@@ -555,6 +613,9 @@ def main():
                 key = f"shared_prefix_hq{hq}"
                 extra[key] = shared_leg(torch, L, wl, W_of, flush, hq)
                 log(f"bench: {key}: {json.dumps(extra[key])}")
+        if "router" in legs:
+            extra["router_gemm"] = router_leg(torch, L)
+            log(f"bench: router_gemm: {json.dumps(extra['router_gemm'])}")
         del flush
         torch.cuda.empty_cache()
         result["extra"] = extra

@@ -55,7 +55,7 @@ size_t router_workspace_bytes(int32_t M, int32_t K, int32_t E);
 
 /*
  * y = x w^T with the split weights.
- *   M, K, E   tokens (>= 1), hidden size (a positive multiple of 32), experts
+ *   M, K, E   tokens (>= 1), hidden size (a positive multiple of 64), experts
  *             (a positive multiple of 16)
  *   x         (device) bf16 [M][K], row-major
  *   w_hi,w_lo (device) bf16 [E][K], row-major (one row per expert), from
@@ -63,8 +63,8 @@ size_t router_workspace_bytes(int32_t M, int32_t K, int32_t E);
  *   y         (device) fp32 [M][E]
  *   workspace (device) >= router_workspace_bytes(M, K, E) bytes, 256-byte
  *             aligned; may be NULL when that size is 0
- * x, w_hi, w_lo 16-byte aligned. The result does not depend on the run: the
- * partial sums of a split K are added in a fixed order.
+ * x, w_hi, w_lo and y 16-byte aligned. The result does not depend on the run:
+ * the partial sums of a split K are added in a fixed order.
  */
 int router_gemm(int32_t M, int32_t K, int32_t E, const void *x, const void *w_hi, const void *w_lo, float *y,
                 void *workspace, size_t workspace_bytes, void *stream);

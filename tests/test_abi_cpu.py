@@ -128,13 +128,13 @@ def test_append_rejects_bad_arguments_before_launch():
 def test_router_shape_checks_on_the_host():
     lib = L.load()
     assert lib.router_workspace_bytes(0, 64, 16) == 0          # M < 1
-    assert lib.router_workspace_bytes(4, 48, 16) == 0          # K not a multiple of 32
+    assert lib.router_workspace_bytes(4, 96, 16) == 0          # K not a multiple of 64
     assert lib.router_workspace_bytes(4, 64, 24) == 0          # E not a multiple of 16
     assert lib.router_workspace_bytes(8192, 7168, 256) == 0    # enough tiles: no split over K
     n = lib.router_workspace_bytes(16, 7168, 256)              # few tokens: K split, fp32 partials
     assert n > 0 and n % (16 * 256 * 4) == 0
-    rc = lib.router_gemm(4, 48, 16, None, None, None, None, None, 0, None)
-    assert rc == L.ATTN_ERR_INVALID_ARG and b"multiple of 32" in lib.attn_last_error()
+    rc = lib.router_gemm(4, 96, 16, None, None, None, None, None, 0, None)
+    assert rc == L.ATTN_ERR_INVALID_ARG and b"multiple of 64" in lib.attn_last_error()
     rc = lib.router_gemm(4, 64, 16, None, None, None, None, None, 0, None)
     assert rc == L.ATTN_ERR_INVALID_ARG and b"non-NULL" in lib.attn_last_error()
     rc = lib.router_gemm(16, 7168, 256, 16, 16, 16, 16, None, 0, None)   # workspace needed

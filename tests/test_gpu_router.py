@@ -55,9 +55,11 @@ def _run(x, w):
 
 
 def _nround(K):
-    """Roundings per output at most: K - 1 additions of the accumulation (in
-    any order), one combine per split of K and S - 1 additions of the splits
-    (S <= K / 256), and slack for the final store."""
+    """Roundings a product term goes through at most: with K split S ways in
+    chunks of c >= 64, c - 1 additions inside its chunk (in any order), one
+    combine of the two products and S - 1 additions of the splits, so
+    c + S <= K + 2 for S = 1 and below K / 2 + 32 + K / 64 otherwise; the
+    bound adds slack."""
     return K + K // 256 + 4
 
 
@@ -81,7 +83,7 @@ def test_split_on_the_device_matches_the_oracle(scale):
     assert np.array_equal(_bits(hi), rh) and np.array_equal(_bits(lo), rl)
 
 
-SHAPES = [(1, 32, 16), (3, 64, 16), (7, 256, 48), (16, 7168, 256), (100, 4096, 128), (129, 2048, 64),
+SHAPES = [(1, 64, 16), (3, 128, 16), (7, 256, 48), (16, 7168, 256), (100, 4096, 128), (129, 2048, 64),
           (128, 1024, 272), (512, 7168, 256), (1000, 4096, 128)]
 
 

@@ -315,10 +315,7 @@ class RouterGemm:
 
     def __init__(self, M, K, E, device="cuda"):
         self.M, self.K, self.E = int(M), int(K), int(E)
-        n = router_workspace_bytes(self.M, self.K, self.E)
-        if n == 0 and load().router_workspace_bytes(self.M, self.K, self.E) == 0:
-            # 0 is also the answer for an invalid shape; router_gemm reports which
-            pass
+        n = router_workspace_bytes(self.M, self.K, self.E)   # 0 also for an invalid shape: router_gemm says which
         self.workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=device) if n else None
         self._ws = (_ptr(self.workspace), ctypes.c_size_t(n)) if n else (None, ctypes.c_size_t(0))
 
