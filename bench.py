@@ -497,6 +497,33 @@ def traffic_probe(torch, L, W, reps=3):
                       "source_hash": source_hash()}), flush=True)
 
 
+def router_probe(torch, L, reps=3):
+    """Launches for rocprofv3 runs of the router GEMM: a plain 1 GiB device
+    copy (the counter scale), then for each router shape in order the weight
+    split once and `reps` GEMM calls, each after a cache flush."""
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        flush.sum()
+        dst.copy_(src)
+    d = "cuda:0"
+    for M, K, E in ROUTER_SHAPES:
+        g = torch.Generator(device=d).manual_seed(M + K + E)
+        x = torch.randn(M, K, generator=g, device=d).to(torch.bfloat16)
+        w = torch.randn(E, K, generator=g, device=d) * 0.02
+        hi = torch.empty(E, K, dtype=torch.bfloat16, device=d)
+        lo = torch.empty_like(hi)
+        L.router_split_weights(w, hi, lo)
+        y = torch.empty(M, E, dtype=torch.float32, device=d)
+        gemm = L.RouterGemm(M, K, E, d)
+        for _ in range(reps):
+            flush.sum()
+            gemm(x, hi, lo, y)
+        torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": src.numel() * 4, "router_shapes": ROUTER_SHAPES, "reps": reps}), flush=True)
+
+
 def traffic_entry(kernel):
     """HBM bytes per launch of `kernel` from committed rocprofv3 counters, only
     if they were taken on the current kernel source."""
@@ -524,6 +551,8 @@ def main():
     ap.add_argument("--trace-steps", type=int, default=256)
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only the launches that the rocprofv3 --pmc runs measure")
+    ap.add_argument("--router-probe", action="store_true",
+                    help="only the router GEMM launches that its rocprofv3 runs measure")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would run its own "
@@ -542,6 +571,9 @@ def main():
 
     if args.traffic_probe:
         traffic_probe(torch, L, W_of(wl.config_lengths(1), 8))
+        return
+    if args.router_probe:
+        router_probe(torch, L)
         return
 
     # ---- headline: uniform-mixed batch, dynamic plan ------------------------

@@ -50,6 +50,7 @@ struct RouterArgs {
     float *y, *part;
     int M, K, E, S, kchunk;
     int mt, et;   // token tiles, expert tiles
+    int upx;      // units per XCD
 };
 
 union RouterLds {
@@ -91,13 +92,14 @@ __global__ __launch_bounds__(kRT) void router_gemm_kernel(RouterArgs a)
     const int r = lane & 15, g = lane >> 4;
     // this wave: k half kg of every step, tokens 64 wm.., experts 32 we..
     const int kg = wave >> 2, wm = (wave >> 1) & 1, we = wave & 1;
-    // Workgroup i runs on XCD i % 8. Consecutive workgroups of one XCD take
-    // the E tiles of one (token tile, k range) unit in turn, so that the
-    // unit's token rows are fetched into that XCD's L2 once and read there by
-    // all of its E tiles; units are numbered token tile first.
+    // Workgroup i runs on XCD i % 8. Units (token tile, k range) are numbered
+    // token tile first and dealt to the XCDs in contiguous runs of a.upx, and
+    // consecutive workgroups of one XCD take the E tiles of one unit in turn:
+    // a unit's token rows, and the weight rows of a k range that several
+    // token tiles share, are then fetched into one XCD's L2 once.
     const int xcd = blockIdx.x % kXcds, q = blockIdx.x / kXcds;
-    const int unit = (q / a.et) * kXcds + xcd;
-    if (unit >= a.mt * a.S)
+    const int unit = xcd * a.upx + q / a.et;
+    if (q / a.et >= a.upx || unit >= a.mt * a.S)
         return;
     const int mt0 = (unit % a.mt) * kTM, et0 = (q % a.et) * kTE;
     const int s = unit / a.mt;
@@ -362,7 +364,8 @@ int router_gemm(int32_t M, int32_t K, int32_t E, const void *x, const void *w_hi
     a.mt = (M + kTM - 1) / kTM;
     a.et = (E + kTE - 1) / kTE;
     const int64_t units = (int64_t)a.mt * S;
-    const dim3 grid((unsigned)((units + kXcds - 1) / kXcds * kXcds * a.et));
+    a.upx = (int)((units + kXcds - 1) / kXcds);
+    const dim3 grid((unsigned)((int64_t)a.upx * kXcds * a.et));
     hipLaunchKernelGGL(router_gemm_kernel, grid, dim3(kRT), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && S > 1) {
