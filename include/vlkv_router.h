@@ -16,8 +16,10 @@
  *     y[m][e] = sum_k x[m][k] w_hi[e][k] + 2^-8 sum_k x[m][k] w_lo[e][k]
  *
  * with each sum accumulated in fp32 by the matrix cores (bf16 x bf16 products
- * are exact in fp32). |w - (w_hi + w_lo/256)| <= 2^-16 |w|, so y differs from
- * the exact fp32-weight product by at most (2^-16 + (K + 2) 2^-24) times
+ * are exact in fp32). |w - (w_hi + w_lo/256)| <= 2^-16 |w|, and a product term
+ * goes through at most K + K/256 + 4 fp32 additions (the accumulation in any
+ * order, the combine and the sums of a split K), so y differs from the exact
+ * fp32-weight product by at most (2^-16 + (K + K/256 + 4) 2^-24) times
  * sum_k |x[m][k] w[e][k]|.
  *
  * Conventions: as in vlkv_attn.h. (device) pointers are HIP device memory,
