@@ -84,7 +84,7 @@ def test_split_on_the_device_matches_the_oracle(scale):
 
 
 SHAPES = [(1, 64, 16), (3, 128, 16), (7, 256, 48), (16, 7168, 256), (100, 4096, 128), (129, 2048, 64),
-          (128, 1024, 272), (512, 7168, 256), (1000, 4096, 128)]
+          (128, 1024, 272), (512, 7168, 256), (1000, 4096, 128), (2, 16384, 32), (64, 1024, 1024)]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
