@@ -141,3 +141,43 @@ def test_router_shape_checks_on_the_host():
     assert rc == L.ATTN_ERR_INVALID_ARG and b"workspace" in lib.attn_last_error()
     assert lib.router_split_weights(None, None, None, -1, None) == L.ATTN_ERR_INVALID_ARG
     assert lib.router_split_weights(None, None, None, 0, None) == L.ATTN_OK
+
+
+def test_binding_checks_tensor_arguments():
+    """The binding rejects a tensor whose dtype, element count, memory or
+    layout differ from the header's before the library sees the pointer."""
+    import torch
+    shape = L.AttnShape(batch=2, num_q_heads=8, num_kv_heads=1, page_size=16, num_pages=4, pt_stride=2,
+                        num_wgs=4)
+    q = torch.zeros(2, 8, 128, dtype=torch.bfloat16)
+    cache = torch.zeros(4, 1, 16, 128, dtype=torch.bfloat16)
+    pt = torch.zeros(2, 2, dtype=torch.int32)
+    ws = torch.zeros(1 << 20, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="q: dtype"):
+        L.attn_decode(shape, q.float(), cache, cache, None, None, pt, 0.1, ws, q.clone())
+    with pytest.raises(ValueError, match="k_cache: 4096 elements, expected 8192"):
+        L.attn_decode(shape, q, cache[:2], cache, None, None, pt, 0.1, ws, q.clone())
+    with pytest.raises(ValueError, match="page_table: 2 elements"):
+        L.attn_decode(shape, q, cache, cache, None, None, pt[0], 0.1, ws, q.clone())
+    with pytest.raises(ValueError, match="out must be contiguous"):
+        L.attn_decode(shape, q, cache, cache, None, None, pt, 0.1, ws, q.transpose(0, 1).contiguous().transpose(0, 1))
+    fp8 = L.AttnShape(**{**shape.__dict__, "kv_dtype": L.ATTN_KV_FP8_E4M3})
+    codes = torch.zeros(4, 1, 16, 128, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="k_scale is required"):
+        L.attn_decode(fp8, q, codes, codes, None, None, pt, 0.1, ws, q.clone())
+    with pytest.raises(ValueError, match="k_cache: dtype"):
+        L.attn_decode(fp8, q, cache, cache, None, None, pt, 0.1, ws, q.clone())
+    with pytest.raises(ValueError, match="q must be in GPU memory"):
+        L.attn_decode(shape, q, cache, cache, None, None, pt, 0.1, ws, q.clone())
+    with pytest.raises(ValueError, match="lengths: 3 elements"):
+        L.attn_plan(shape, torch.zeros(3, dtype=torch.int32), pt, ws)
+    g = L.RouterGemm(8192, 7168, 256, "cpu")          # no workspace at this shape
+    x = torch.zeros(8192, 7168, dtype=torch.bfloat16)
+    w = torch.zeros(256, 7168, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="y: dtype"):
+        g(x, w, w, torch.zeros(8192, 256, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="x must be in GPU memory"):
+        g(x, w, w, torch.zeros(8192, 256, dtype=torch.float32))
+    with pytest.raises(ValueError, match="w_hi: 9 elements"):
+        L.router_split_weights(torch.zeros(10), torch.zeros(9, dtype=torch.bfloat16),
+                               torch.zeros(10, dtype=torch.bfloat16))

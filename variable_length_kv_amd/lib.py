@@ -116,6 +116,76 @@ def _ptr(t):
     return ctypes.c_void_p(int(t))
 
 
+_BF16 = (torch.bfloat16,)
+_HALFWORD = (torch.bfloat16, torch.int16, torch.uint16)
+_FP8 = (torch.uint8, torch.float8_e4m3fn)
+_I32 = (torch.int32,)
+_F32 = (torch.float32,)
+
+
+def _need(t, name, dtypes, numel, optional=False):
+    """A tensor argument laid out as the C header says: one of `dtypes`, exactly
+    `numel` elements, contiguous. Raises ValueError before anything is
+    enqueued; an int (a raw device address) is passed through unchecked. Where
+    the tensor lives is checked apart (_on_gpu), after every argument's
+    layout."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        return
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {' or '.join(str(d) for d in dtypes)}")
+    if t.numel() != numel:
+        raise ValueError(f"{name}: {t.numel()} elements, expected {numel}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _on_gpu(**tensors):
+    for name, t in tensors.items():
+        if isinstance(t, torch.Tensor) and t.device.type != "cuda":
+            raise ValueError(f"{name} must be in GPU memory")
+
+
+def _need_step(shape, q=None, k_cache=None, v_cache=None, k_scale=None, v_scale=None, page_table=None,
+               lengths=None, out=None, lse=None, decode=True, plan=True):
+    B, Hq, Hkv, D = shape.batch, shape.num_q_heads, shape.num_kv_heads, shape.head_dim
+    if plan:
+        _need(lengths, "lengths", _I32, B)
+        _need(page_table, "page_table", _I32, B * shape.pt_stride, optional=shape.mode != ATTN_SHARED)
+    if decode:
+        fp8 = shape.kv_dtype == ATTN_KV_FP8_E4M3
+        _need(q, "q", _BF16, B * Hq * D)
+        cache = shape.num_pages * Hkv * shape.page_size * D
+        _need(k_cache, "k_cache", _FP8 if fp8 else _BF16, cache)
+        _need(v_cache, "v_cache", _FP8 if fp8 else _BF16, cache)
+        _need(k_scale, "k_scale", _F32, B * Hkv, optional=not fp8)
+        _need(v_scale, "v_scale", _F32, B * Hkv, optional=not fp8)
+        _need(page_table, "page_table", _I32, B * shape.pt_stride)
+    if decode or out is not None:
+        _need(out, "out", _BF16, B * Hq * D)
+        _need(lse, "lse", _F32, B * Hq, optional=True)
+    _on_gpu(q=q, k_cache=k_cache, v_cache=v_cache, k_scale=k_scale, v_scale=v_scale, page_table=page_table,
+            lengths=lengths, out=out, lse=lse)
+
+
+def _need_append(sh, k_new, v_new, positions, page_table, k_cache, v_cache, k_scale, v_scale):
+    fp8 = sh.kv_dtype == ATTN_KV_FP8_E4M3
+    _need(k_new, "k_new", _BF16, sh.batch * sh.num_kv_heads * sh.head_dim)
+    _need(v_new, "v_new", _BF16, sh.batch * sh.num_kv_heads * sh.head_dim)
+    _need(positions, "positions", _I32, sh.batch)
+    _need(page_table, "page_table", _I32, sh.batch * sh.pt_stride)
+    _need(k_scale, "k_scale", _F32, sh.batch * sh.num_kv_heads, optional=not fp8)
+    _need(v_scale, "v_scale", _F32, sh.batch * sh.num_kv_heads, optional=not fp8)
+    cache = sh.num_pages * sh.num_kv_heads * sh.page_size * sh.head_dim
+    _need(k_cache, "k_cache", _FP8 if fp8 else _BF16, cache)
+    _need(v_cache, "v_cache", _FP8 if fp8 else _BF16, cache)
+    _on_gpu(k_new=k_new, v_new=v_new, positions=positions, page_table=page_table, k_cache=k_cache,
+            v_cache=v_cache, k_scale=k_scale, v_scale=v_scale)
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -163,12 +233,14 @@ def attn_device_cu_count(device: int = 0) -> int:
 
 
 def attn_plan(shape, lengths, page_table, workspace, stream=None) -> None:
+    _need_step(shape, lengths=lengths, page_table=page_table, decode=False)
     _check(load().attn_plan(_shape(shape), _ptr(lengths), _ptr(page_table), _ptr(workspace),
                             workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def attn_decode(shape, q, k_cache, v_cache, k_scale, v_scale, page_table, sm_scale, workspace, out,
                 lse=None, stream=None) -> None:
+    _need_step(shape, q, k_cache, v_cache, k_scale, v_scale, page_table, out=out, lse=lse, plan=False)
     _check(load().attn_decode(_shape(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
                               _ptr(v_scale), _ptr(page_table), float(sm_scale), _ptr(workspace),
                               workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
@@ -176,6 +248,7 @@ def attn_decode(shape, q, k_cache, v_cache, k_scale, v_scale, page_table, sm_sca
 
 
 def attn_combine(shape, workspace, out, lse=None, stream=None) -> None:
+    _need_step(shape, out=out, lse=lse, decode=False, plan=False)
     _check(load().attn_combine(_shape(shape), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                _ptr(out), _ptr(lse), _stream(stream)))
 
@@ -187,6 +260,7 @@ def attn_workspace_init(shape, workspace, stream=None) -> None:
 
 def attn_step(shape, q, k_cache, v_cache, k_scale, v_scale, page_table, lengths, sm_scale, workspace, out,
               lse=None, stream=None) -> None:
+    _need_step(shape, q, k_cache, v_cache, k_scale, v_scale, page_table, lengths, out, lse)
     _check(load().attn_step(_shape(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
                             _ptr(page_table), _ptr(lengths), float(sm_scale), _ptr(workspace),
                             workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(stream)))
@@ -195,6 +269,7 @@ def attn_step(shape, q, k_cache, v_cache, k_scale, v_scale, page_table, lengths,
 def attn_append_kv(shape, k_new, v_new, positions, page_table, k_cache, v_cache, k_scale=None, v_scale=None,
                    workspace=None, stream=None) -> None:
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _need_append(shape, k_new, v_new, positions, page_table, k_cache, v_cache, k_scale, v_scale)
     _check(load().attn_append_kv(_shape(shape), _ptr(k_new), _ptr(v_new), _ptr(positions), _ptr(page_table),
                                  _ptr(k_scale), _ptr(v_scale), _ptr(k_cache), _ptr(v_cache), _ptr(workspace),
                                  nbytes, _stream(stream)))
@@ -261,6 +336,7 @@ class Attention:
 
     def fused_step(self, q, k_cache, v_cache, page_table, lengths, sm_scale, out, lse=None, k_scale=None,
                    v_scale=None, stream=None):
+        _need_step(self.shape, q, k_cache, v_cache, k_scale, v_scale, page_table, lengths, out, lse)
         _check(load().attn_step(self._cshape, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
                                 _ptr(v_scale), _ptr(page_table), _ptr(lengths), float(sm_scale), self._ws[0],
                                 self._ws[1], _ptr(out), _ptr(lse), _stream(stream)))
@@ -284,6 +360,7 @@ class Attention:
 
     def append_kv(self, k_new, v_new, positions, page_table, k_cache, v_cache, k_scale=None, v_scale=None,
                   stream=None):
+        _need_append(self.shape, k_new, v_new, positions, page_table, k_cache, v_cache, k_scale, v_scale)
         _check(load().attn_append_kv(self._cshape, _ptr(k_new), _ptr(v_new), _ptr(positions), _ptr(page_table),
                                      _ptr(k_scale), _ptr(v_scale), _ptr(k_cache), _ptr(v_cache), self._ws[0],
                                      self._ws[1], _stream(stream)))
@@ -300,8 +377,10 @@ class Attention:
 def router_split_weights(w, w_hi, w_lo, stream=None):
     """w_hi = bf16(w), w_lo = bf16(256 (w - w_hi)) on the device (tensors: w
     fp32, w_hi / w_lo bf16 or int16 of w's size)."""
-    if w.numel() != w_hi.numel() or w.numel() != w_lo.numel():
-        raise ValueError("w, w_hi and w_lo must have the same number of elements")
+    _need(w, "w", _F32, w.numel())
+    _need(w_hi, "w_hi", _HALFWORD, w.numel())
+    _need(w_lo, "w_lo", _HALFWORD, w.numel())
+    _on_gpu(w=w, w_hi=w_hi, w_lo=w_lo)
     _check(load().router_split_weights(_ptr(w), _ptr(w_hi), _ptr(w_lo), ctypes.c_int64(w.numel()),
                                        _stream(stream)))
 
@@ -320,8 +399,10 @@ class RouterGemm:
         self._ws = (_ptr(self.workspace), ctypes.c_size_t(n)) if n else (None, ctypes.c_size_t(0))
 
     def __call__(self, x, w_hi, w_lo, y, stream=None):
-        if x.shape != (self.M, self.K) or w_hi.shape != (self.E, self.K) or w_lo.shape != (self.E, self.K) \
-                or y.shape != (self.M, self.E):
-            raise ValueError("router_gemm: x [M,K], w_hi/w_lo [E,K], y [M,E]")
+        _need(x, "x", _BF16, self.M * self.K)
+        _need(w_hi, "w_hi", _HALFWORD, self.E * self.K)
+        _need(w_lo, "w_lo", _HALFWORD, self.E * self.K)
+        _need(y, "y", _F32, self.M * self.E)
+        _on_gpu(x=x, w_hi=w_hi, w_lo=w_lo, y=y)
         _check(load().router_gemm(self.M, self.K, self.E, _ptr(x), _ptr(w_hi), _ptr(w_lo), _ptr(y), self._ws[0],
                                   self._ws[1], _stream(stream)))
