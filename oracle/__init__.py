@@ -7,9 +7,12 @@ package imports nothing from the product.
 
 ``decode`` is the fp64 definition of one decode-attention step (C, in
 ``oracle.c``); ``plan`` is the integer tile-plan specification the GPU planner
-must reproduce byte for byte; ``append_kv`` writes one new token per request
-into a paged cache (``e4m3fn_encode`` is its fp8 rounding); ``brute`` holds an independent NumPy two-pass
-softmax used to pin ``decode`` on tiny inputs. Inputs are plain host arrays
+must reproduce byte for byte, and ``plan_shared`` that of the prefix-shared
+plan; ``append_kv`` writes one new token per request into a paged cache
+(``e4m3fn_encode`` is its fp8 rounding); ``router_split`` and ``router_gemm``
+define the router GEMM with fp32 weights split into two bf16 parts
+(``bf16_rne`` is their rounding); ``brute`` holds an independent NumPy
+two-pass softmax used to pin ``decode`` on tiny inputs. Inputs are plain host arrays
 (numpy, or CPU torch tensors), duck-typed on the attribute names of a decode
 step: B, Hq, Hkv, D, P, num_pages, kv_dtype, q, k_cache, v_cache, k_scale,
 v_scale, page_table, lengths, sm_scale.
