@@ -136,8 +136,6 @@ WsLayout ws_layout(const Shape &s)
     L.req_shared = take(sizeof(int32_t) * nr);
     L.req_member = take(sizeof(int32_t) * nr);
     L.req_own = take(sizeof(int32_t) * nr);
-    L.share = take(sizeof(int32_t) * nr);
-    L.len_req = take(sizeof(int32_t) * nr);
     L.counters = take(sizeof(int32_t) * nbg);
     L.part_lse = take(sizeof(float) * L.max_slots * L.slot_rows);
     L.part_o = take(sizeof(float) * L.max_slots * L.slot_rows * s.D);
@@ -259,8 +257,6 @@ static int enqueue_plan(const Shape &s, const WsLayout &L, const int32_t *length
     a.req_shared = at<int32_t>(workspace, L.req_shared);
     a.req_member = at<int32_t>(workspace, L.req_member);
     a.req_own = at<int32_t>(workspace, L.req_own);
-    a.share = at<int32_t>(workspace, L.share);
-    a.len_req = at<int32_t>(workspace, L.len_req);
     a.B = s.B;
     a.Hkv = s.Hkv;
     a.G = s.G;

@@ -200,14 +200,16 @@ __global__ __launch_bounds__(kPT) void plan_kernel(PlanArgs a)
 
 
 // Group of request b (mode 2): its leader, member count m and the group's
-// shared tokens Ls (0 when m < 2). rs is the start of b's run.
-__device__ __forceinline__ void group_of(const PlanArgs &a, int R, int b, int rs, int &leader, int &m, int &Ls)
+// shared tokens Ls (0 when m < 2). rs is the start of b's run; share[] holds
+// each request's tokens shared with the previous one.
+__device__ __forceinline__ void group_of(const int32_t *share, int B, int R, int b, int rs, int &leader, int &m,
+                                         int &Ls)
 {
     leader = rs + (b - rs) / R * R;
     m = 1;
     Ls = INT32_MAX;
-    while (m < R && leader + m < a.B) {
-        const int sh = a.share[leader + m];
+    while (m < R && leader + m < B) {
+        const int sh = share[leader + m];
         if (sh == 0)
             break;
         Ls = min(Ls, sh);
@@ -217,11 +219,14 @@ __device__ __forceinline__ void group_of(const PlanArgs &a, int R, int b, int rs
         Ls = 0;
 }
 
-// Mode 2: prefix-shared pages. Intermediate arrays live in the workspace; all
-// threads are in one workgroup, so barriers order them.
+// Mode 2: prefix-shared pages. All threads are in one workgroup; the
+// per-request intermediates (shared tokens, validated lengths) stay in LDS,
+// so the phases that read other threads' entries cost no memory round trips.
 __global__ __launch_bounds__(kST) void plan_shared_kernel(PlanArgs a)
 {
     __shared__ int32_t tp_lds[kMaxBatch + 1];   // item tiles prefix, when at most kMaxBatch items
+    __shared__ int32_t share_lds[kMaxBatch];    // tokens shared with the previous request
+    __shared__ int32_t len_lds[kMaxBatch];      // validated lengths
     __shared__ int scan_lds[kSW];
     __shared__ int red_lds[2 * kSW];
     const int tid = threadIdx.x;
@@ -231,46 +236,75 @@ __global__ __launch_bounds__(kST) void plan_shared_kernel(PlanArgs a)
     const int b0 = min(a.B, tid * cA), b1 = min(a.B, b0 + cA);
 
     // 1) tokens shared with the previous request: leading page slots with the
-    //    same valid id, capped by both lengths, whole tiles. It reads only the
-    //    inputs, so it goes first. Lane l of a wave
+    //    same valid id, capped by both lengths, whole tiles; and the validated
+    //    lengths (out-of-range lengths count as 0 and set the status bit). It
+    //    reads only the inputs, so it goes first. Lane l of a wave
     //    compares slots 4l..4l+3 (256 consecutive slots per step, coalesced);
     //    a ballot over the lanes whose 4 slots all agree finds the first
     //    mismatch. Each of the 16 waves takes kNB requests at a time
-    //    (b = wave + 16 k), so all their loads share one round trip per step;
+    //    (b = wave + 16 k), so all their loads share one round trip per step,
+    //    and the first step's loads go out together with the lengths';
     //    the round trips, not the bytes, are what this phase costs (a wave
     //    holds at most 63 loads in flight, hence the 16 waves).
+    int mx = 0, st = 0;
     {
         constexpr int kNB = 8, kSub = 4, kSpan = 64 * kSub;
         const int wave = tid >> 6, lane = tid & 63;
         for (int base = wave; base < a.B; base += kSW * kNB) {
             int c[kNB], n[kNB], lmin[kNB];
             bool done[kNB];
+            int x[kNB][kSub], y[kNB][kSub];
+            // the first step's slots of rows b and b - 1 do not depend on the
+            // lengths: their loads go out with the lengths' (one round trip)
 #pragma unroll
             for (int k = 0; k < kNB; ++k) {
-                // branch-free, in-bounds loads (all of them in one round trip)
+                const int b = base + kSW * k;
+                const int32_t *ra = a.page_table + (size_t)b * a.pt_stride;
+#pragma unroll
+                for (int i = 0; i < kSub; ++i) {
+                    const int j = kSub * lane + i;
+                    x[k][i] = -1;
+                    y[k][i] = -2;
+                    if (b > 0 && b < a.B && j < a.pt_stride) {
+                        x[k][i] = ra[j];
+                        y[k][i] = ra[j - a.pt_stride];
+                    }
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < kNB; ++k) {
+                // branch-free, in-bounds loads
                 const int b = base + kSW * k;
                 const int ia = max(min(b, a.B - 1), 0), ip = max(ia - 1, 0);
                 int la = a.lengths[ia], lp = a.lengths[ip];
-                la = (la < 0 || (int64_t)la > limit) ? 0 : la;   // validated as in step 1
+                if (b < a.B && (la < 0 || (int64_t)la > limit))
+                    st = 1;
+                la = (la < 0 || (int64_t)la > limit) ? 0 : la;
                 lp = (lp < 0 || (int64_t)lp > limit) ? 0 : lp;
+                if (b < a.B) {
+                    mx = max(mx, la);
+                    if (lane == 0)
+                        len_lds[b] = la;
+                }
                 lmin[k] = min(la, lp);
                 c[k] = 0;
                 n[k] = (b > 0 && b < a.B) ? (lmin[k] + a.P - 1) / a.P : 0;
                 done[k] = n[k] == 0;
             }
-            for (;;) {
-                int x[kNB][kSub], y[kNB][kSub];
+            for (bool first = true;; first = false) {
+                if (!first) {
 #pragma unroll
-                for (int k = 0; k < kNB; ++k) {
-                    const int32_t *ra = a.page_table + (size_t)(base + kSW * k) * a.pt_stride;
+                    for (int k = 0; k < kNB; ++k) {
+                        const int32_t *ra = a.page_table + (size_t)(base + kSW * k) * a.pt_stride;
 #pragma unroll
-                    for (int i = 0; i < kSub; ++i) {
-                        x[k][i] = -1;
-                        y[k][i] = -2;
-                        const int j = c[k] + kSub * lane + i;
-                        if (!done[k] && j < n[k]) {
-                            x[k][i] = ra[j];
-                            y[k][i] = ra[j - a.pt_stride];
+                        for (int i = 0; i < kSub; ++i) {
+                            x[k][i] = -1;
+                            y[k][i] = -2;
+                            const int j = c[k] + kSub * lane + i;
+                            if (!done[k] && j < n[k]) {
+                                x[k][i] = ra[j];
+                                y[k][i] = ra[j - a.pt_stride];
+                            }
                         }
                     }
                 }
@@ -282,7 +316,9 @@ __global__ __launch_bounds__(kST) void plan_shared_kernel(PlanArgs a)
                     int m = 0;   // this lane's slots that agree (slots past n do not)
 #pragma unroll
                     for (int i = 0; i < kSub; ++i)
-                        m |= (x[k][i] == y[k][i] && x[k][i] >= 0 && x[k][i] < a.num_pages) << i;
+                        m |= (c[k] + kSub * lane + i < n[k] && x[k][i] == y[k][i] && x[k][i] >= 0 &&
+                              x[k][i] < a.num_pages)
+                             << i;
                     const uint64_t full = __builtin_amdgcn_ballot_w64(m == (1 << kSub) - 1);
                     int run = kSpan;
                     if (full != ~0ull) {
@@ -303,48 +339,39 @@ __global__ __launch_bounds__(kST) void plan_shared_kernel(PlanArgs a)
                     const int b = base + kSW * k;
                     if (b < a.B) {
                         const int64_t t = b > 0 ? min((int64_t)c[k] * a.P, (int64_t)lmin[k]) : 0;
-                        a.share[b] = (int)(t / a.T * a.T);
+                        share_lds[b] = (int)(t / a.T * a.T);
                     }
                 }
             }
         }
     }
 
-    // 2) validated lengths
-    int mx = 0, st = 0;
-    for (int b = b0; b < b1; ++b) {
-        int L = a.lengths[b];
-        if (L < 0 || (int64_t)L > limit) {
-            st = 1;
-            L = 0;
-        }
-        a.len_req[b] = L;
-        mx = max(mx, L);
-    }
+    // 2) the largest length and the status bit (the barriers of the reduction
+    //    also publish share_lds and len_lds)
     int maxle, status;
-    block_max_or<kST>(mx, st, red_lds, &maxle, &status);   // its barriers publish len_req and share
+    block_max_or<kST>(mx, st, red_lds, &maxle, &status);
 
     // 3) runs (start at b = 0 and wherever share = 0), groups of R, and the
     //    item and tile counts of each thread's requests
     int last_start = -1;
     for (int b = b0; b < b1; ++b)
-        if (b == 0 || a.share[b] == 0)
+        if (b == 0 || share_lds[b] == 0)
             last_start = b;
     const int carry = block_excl_max_scan<kST>(last_start, -1, scan_lds);
     int nitems = 0, ntiles = 0;
     {
         int rs = carry;
         for (int b = b0; b < b1; ++b) {
-            if (b == 0 || a.share[b] == 0)
+            if (b == 0 || share_lds[b] == 0)
                 rs = b;
             int leader, m, Ls;
-            group_of(a, R, b, rs, leader, m, Ls);
+            group_of(share_lds, a.B, R, b, rs, leader, m, Ls);
             if (b == leader && m >= 2) {
                 ++nitems;
                 ntiles += (Ls + a.T - 1) / a.T;
             }
             ++nitems;
-            ntiles += (a.len_req[b] - Ls + a.T - 1) / a.T;
+            ntiles += (len_lds[b] - Ls + a.T - 1) / a.T;
         }
     }
     int n_items, total;
@@ -355,10 +382,10 @@ __global__ __launch_bounds__(kST) void plan_shared_kernel(PlanArgs a)
     {
         int i = ibase, t = tbase, rs = carry;
         for (int b = b0; b < b1; ++b) {
-            if (b == 0 || a.share[b] == 0)
+            if (b == 0 || share_lds[b] == 0)
                 rs = b;
             int leader, m, Ls;
-            group_of(a, R, b, rs, leader, m, Ls);
+            group_of(share_lds, a.B, R, b, rs, leader, m, Ls);
             if (b == leader && m >= 2) {
                 a.item_req[i] = b;
                 a.item_start[i] = 0;
@@ -371,7 +398,7 @@ __global__ __launch_bounds__(kST) void plan_shared_kernel(PlanArgs a)
                     tp_lds[i + 1] = t;
                 ++i;
             }
-            const int Lb = a.len_req[b];
+            const int Lb = len_lds[b];
             a.item_req[i] = b;
             a.item_start[i] = Ls;
             a.len_eff[i] = Lb - Ls;

@@ -34,7 +34,7 @@ __host__ __device__ constexpr int shared_group(int G) { return G >= kMaxGroup ? 
 // and wg_start_b are indexed by item, and the item_* / req_* regions exist.
 struct WsLayout {
     size_t header, len_eff, tiles_prefix, seg_prefix, first_wg, wg_begin, wg_start_b;
-    size_t item_req, item_start, item_m, item_solo, req_shared, req_member, req_own, share, len_req;
+    size_t item_req, item_start, item_m, item_solo, req_shared, req_member, req_own;
     size_t counters, part_lse, part_o, total;
     int64_t max_slots, max_items;
     int slot_rows;   // query rows per partial slot
@@ -60,7 +60,7 @@ struct PlanArgs {
     const int32_t *page_table;   // mode 2 only
     int32_t *header, *len_eff, *tiles_prefix, *seg_prefix, *first_wg, *wg_begin, *wg_start_b;
     // mode 2 only
-    int32_t *item_req, *item_start, *item_m, *item_solo, *req_shared, *req_member, *req_own, *share, *len_req;
+    int32_t *item_req, *item_start, *item_m, *item_solo, *req_shared, *req_member, *req_own;
     int B, Hkv, G, P, pt_stride, num_pages, T, W, mode, S;
 };
 
