@@ -299,15 +299,15 @@ def shared_leg(torch, L, wl, W_of, flush, Hq):
     prompt (its 128 pages aliased in their page tables), each request with its
     own suffix of U[64, 2048] tokens; 8 kv heads, page 64, bf16. The dynamic
     plan (single launch) reads every request's prefix; the shared plan
-    (ATTN_SHARED, three launches) reads a group's prefix once per 16/G
-    requests. Logical bytes count every request's rows; read bytes count the
+    (ATTN_SHARED, three launches) reads a group's prefix once per 32/G
+    requests at G >= 8, 16/G below. Logical bytes count every request's rows; read bytes count the
     rows the shared plan's items read."""
     lengths, groups = wl.shared_prefix_lengths(16, 4, 8192, 64, 2048, 64, seed=0)
     c = wl.make_shared_case("shared", lengths, groups, Hq=Hq, Hkv=8, P=64, seed=0)
     W = W_of(c.lengths, c.Hkv)
     r = Runner(c, torch, L, W)
     per_tok = 2 * c.Hkv * c.D * c.elem_bytes
-    entry = {"requests": c.B, "q_heads": Hq, "kv_heads": c.Hkv, "requests_per_shared_pass": max(1, 16 // c.G),
+    entry = {"requests": c.B, "q_heads": Hq, "kv_heads": c.Hkv, "requests_per_shared_pass": max(1, (32 if c.G >= 8 else 16) // c.G),
              "logical_gb": round(c.kv_bytes / 1e9, 4), "num_wgs": W}
     a = r.attention(L.ATTN_DYNAMIC)
     t_dyn = per_step_flushed(r, a, 30, 5, torch, flush, True)

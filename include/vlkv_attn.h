@@ -136,10 +136,11 @@ int attn_device_cu_count(int device, int32_t *cus);
  * inference kernels, sec. "Why Tencent HPC matters for online model
  * serving"]): request b shares with b-1 the leading page slots that hold the
  * same valid page id, capped by both lengths and rounded down to whole tiles.
- * Runs of adjacent sharing requests are cut into groups of R = 16 / G
- * (G = Hq/Hkv; one pass holds 16 query rows); a group of two or more reads its
- * common prefix once, as one item whose query rows are the members' heads, and
- * each request keeps an item for its remaining tokens. The partition above then
+ * Runs of adjacent sharing requests are cut into groups of R = 32 / G for
+ * G = Hq/Hkv >= 8 and R = 16 / G below (one pass holds 32 or 16 query rows);
+ * a group of two or more reads its common prefix once, as one item whose query
+ * rows are the members' heads, and each request keeps an item for its
+ * remaining tokens. The partition above then
  * runs over (item, kv head, tile) units. Results equal the other modes' up to
  * the order of the softmax merge. The plan's arrays are over items
  * (attn_read_plan, attn_read_plan_items).

@@ -359,8 +359,9 @@ int oracle_plan(int32_t mode, int32_t B, int32_t Hkv, int32_t P, int32_t pt_stri
  *    id valid (0 <= id < num_pages); share_b = min(c P, Le_b, Le_{b-1}) rounded
  *    down to a multiple of T. share_0 = 0.
  * 3. Runs: a run starts at b = 0 and at every b with share_b = 0. A run is cut,
- *    from its start, into groups of R = max(1, 16 / G) consecutive requests
- *    (16 query rows per pass: R requests times G query heads of one kv head).
+ *    from its start, into groups of R consecutive requests: R = 32 / G for
+ *    G >= 8 (two MFMA column blocks of 16 query rows per pass), R = 16 / G
+ *    below (one block); R requests times G query heads of one kv head.
  *    A group with m >= 2 members shares Ls = min of share over its members
  *    other than the first (its pages agree with the first member's there).
  * 4. Items, in request order: a group leader with m >= 2 first emits the
@@ -385,7 +386,7 @@ int oracle_plan_shared(int32_t B, int32_t Hkv, int32_t G, int32_t P, int32_t pt_
 {
     if (B < 0 || Hkv <= 0 || G <= 0 || P <= 0 || pt_stride < 0 || num_pages <= 0 || T <= 0 || W <= 0)
         return ORACLE_EINVAL;
-    const int32_t R = G >= 16 ? 1 : 16 / G;
+    const int32_t R = G >= 32 ? 1 : G >= 8 ? 32 / G : 16 / G;
     int32_t status = 0;
     int64_t maxle = 0;
     int32_t *Le = calloc((size_t)(B > 0 ? B : 1), sizeof *Le);

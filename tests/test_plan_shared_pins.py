@@ -114,7 +114,7 @@ def test_random_against_token_brute_force(seed):
     B, pt_stride = pt.shape
     limit = pt_stride * P
     Le = [int(L) if 0 <= L <= limit else 0 for L in lengths]
-    R = max(1, 16 // G)
+    R = max(1, (32 if G >= 8 else 16) // G)
     p = oracle.plan_shared(lengths, pt, Hkv, G, P, num_pages, T, W)
     share = _brute_share(pt, Le, P, T, num_pages)
     items, req_shared, req_member, req_own = _expected_items(Le, share, R)

@@ -341,7 +341,9 @@ static int enqueue_decode(const Shape &s, const WsLayout &L, const void *q, cons
     a.slot_rows = L.slot_rows;
     a.scale_log2 = sm_scale * 1.4426950408889634f;
     const int grid = s.mode == ATTN_STATIC ? s.B * s.Hkv * s.S : s.W;
-    const int src = s.mode == ATTN_STATIC ? SRC_STATIC : s.mode == ATTN_SHARED ? SRC_SHARED : SRC_DYNAMIC;
+    const int src = s.mode == ATTN_STATIC   ? SRC_STATIC
+                    : s.mode == ATTN_SHARED ? (shared_blocks(s.G) == 2 ? SRC_SHARED_WIDE : SRC_SHARED)
+                                            : SRC_DYNAMIC;
     const hipError_t e = launch_decode(a, src, s.kv_fp8, grid, st);
     if (e != hipSuccess)
         return hip_fail(e, "decode launch");

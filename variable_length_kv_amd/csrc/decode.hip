@@ -125,7 +125,9 @@ __device__ __forceinline__ int len_valid(const DecodeArgs *a, int b)
     return (L < 0 || (int64_t)L > (int64_t)a->pt_stride * a->P) ? 0 : L;
 }
 
-// Registers of one in-flight slice (fp8 uses k[0..1], v[0..1]).
+// Registers of one in-flight slice (fp8 uses k[0..1], v[0..1]) and q of the
+// first column block of 16 query rows (a second block's q is loaded when its
+// segment starts: carrying it in every slot would not fit the registers).
 struct Slot {
     u32x4 k[4];
     u32x4 v[4];
@@ -147,7 +149,7 @@ struct Meta {
     int first_off;  // single launch, dynamic: slot offset of that first segment
     int m;       // query requests b, b+1, .., b+m-1 (more than one: a shared prefix)
     int tbase;   // first token of the item (0 unless a request's own rest)
-    float ksc, vsc;
+    float ksc, vsc;   // fp8 scales of the first column block (per row in SRC_SHARED)
 };
 
 // Walks a workgroup's blocks in order. SRC_DYNAMIC / SRC_FUSED_DYNAMIC /
@@ -157,7 +159,7 @@ struct Meta {
 template <int SRC>
 struct Walker {
     static constexpr bool kFused = SRC == SRC_FUSED_DYNAMIC || SRC == SRC_FUSED_STATIC;
-    static constexpr bool kShared = SRC == SRC_SHARED;
+    static constexpr bool kShared = is_shared(SRC);
     static constexpr bool kPlanned = SRC == SRC_DYNAMIC || kShared;   // ranges from attn_plan's arrays
     static constexpr bool kDyn = kPlanned || SRC == SRC_FUSED_DYNAMIC;
 
@@ -486,20 +488,21 @@ __device__ __forceinline__ void merge_partials(const float *part_o, const float 
     }
 }
 
+template <int NCB>
 struct DecodeLds {
     union {
-        float acc[kWaves][kMaxGroup][kLdsRow];  // per-wave states at a segment's end
+        float acc[kWaves][kMaxGroup * NCB][kLdsRow];  // per-wave states at a segment's end
         struct {
             int32_t tp[kMaxBatch + 1];          // single launch: tiles prefix (prologue only)
             int32_t len[kMaxBatch];             // and validated lengths
         };
     };
-    float m[kWaves][kMaxGroup];
-    float l[kWaves][kMaxGroup];
-    float e[kWaves][kMaxGroup];
+    float m[kWaves][kMaxGroup * NCB];
+    float l[kWaves][kMaxGroup * NCB];
+    float e[kWaves][kMaxGroup * NCB];
     int red[2 * kWaves];
     int flag;
-    float vs[kMaxGroup];   // SRC_SHARED: V scale of each query row
+    float vs[kMaxGroup * NCB];   // SRC_SHARED: V scale of each query row
 };
 
 template <int SRC, int KVFP8>
@@ -507,14 +510,17 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
 {
     constexpr bool kFused = SRC == SRC_FUSED_DYNAMIC || SRC == SRC_FUSED_STATIC;
     const int w = blockIdx.x;
-    if ((SRC == SRC_DYNAMIC || SRC == SRC_SHARED) && w >= ldc(a.header, H_WEFF))
+    if ((SRC == SRC_DYNAMIC || is_shared(SRC)) && w >= ldc(a.header, H_WEFF))
         return;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int row = lane & 15;   // MFMA row / column within a 16x16 tile
     const int grp = lane >> 4;   // MFMA row group
 
-    __shared__ __attribute__((aligned(16))) DecodeLds lds;
+    // Column blocks of 16 query rows: a shared prefix item stacks up to
+    // 32 / G requests' heads in two blocks that read each K/V slice once.
+    constexpr int NCB = SRC == SRC_SHARED_WIDE ? 2 : 1;
+    __shared__ __attribute__((aligned(16))) DecodeLds<NCB> lds;
 
     const int G = a.G;
     constexpr int D = kHeadDim;
@@ -614,15 +620,23 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
     // groups; l_run is this lane's partial sum, reduced at segment end.
     // l_run sums the bf16-rounded weights that multiply V (normalises o exactly
     // like P.V); e_run sums the unrounded fp32 weights (gives an accurate lse).
-    float m_run = -INFINITY, l_run = 0.f, e_run = 0.f, sc = a.scale_log2, vsc_run = 1.f;
-    f32x4 acc[8];
-    u32x4 qreg[4];
+    // One set per column block.
+    float m_run[NCB], l_run[NCB], e_run[NCB], sc[NCB], vsc_run[NCB];
+    f32x4 acc[NCB][8];
+    u32x4 qreg[NCB][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < NCB; ++cb) {
+        m_run[cb] = -INFINITY;
+        l_run[cb] = e_run[cb] = 0.f;
+        sc[cb] = a.scale_log2;
+        vsc_run[cb] = 1.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        qreg[i] = u32x4{0u, 0u, 0u, 0u};
+        for (int i = 0; i < 8; ++i)
+            acc[cb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            qreg[cb][i] = u32x4{0u, 0u, 0u, 0u};
+    }
 
     int bad_page = 0;
     // this lane's byte offset inside a 16-row slice: row (token) and 16-byte column group
@@ -633,36 +647,43 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
     // for an empty or invalid slice (then from page 0, which always exists, and
     // never used), so the number of vector loads between any two points of the
     // pipeline is fixed and the wait before each compute covers its own slot only.
+    // q of query rows 16 cb .. 16 cb + 15 of a segment: row r is head r % G of
+    // request b + r / G (a shared prefix stacks m requests; rows past m G
+    // read head 0 and are zeroed at use); fp8: the scales of each row's request
+    auto load_q = [&](u32x4 (&q)[4], const Meta &mt, int cb, float &ksc, float &vsc) {
+        const int rr = 16 * cb + row;
+        const int hrow = rr < mt.m * G ? rr : 0;
+        int qb = mt.b, qh = hrow;
+        if (is_shared(SRC)) {
+            const int mem = hrow / G;
+            qb += mem;
+            qh = hrow - mem * G;
+        }
+        const uint16_t *qp = a.q + ((size_t)qb * a.Hq + (size_t)mt.g * G + qh) * D;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int d0 = KVFP8 ? 16 * grp + 64 * (kk >> 1) + 8 * (kk & 1) : 32 * kk + 8 * grp;
+            q[kk] = *reinterpret_cast<const u32x4 *>(qp + d0);
+        }
+        if (KVFP8) {
+            if (is_shared(SRC)) {   // per row
+                ksc = a.k_scale[(size_t)qb * a.Hkv + mt.g];
+                vsc = a.v_scale[(size_t)qb * a.Hkv + mt.g];
+            } else {
+                ksc = ldc(a.k_scale, (size_t)mt.b * a.Hkv + mt.g);
+                vsc = ldc(a.v_scale, (size_t)mt.b * a.Hkv + mt.g);
+            }
+        }
+    };
+
     auto issue = [&](Slot &s, Meta &mt) {
         mt = wk.next();
         if (mt.valid && mt.first) {
             // q of (b, g) as the B operand: head = row. Branch-free: rows >= G
             // read head 0 and are zeroed when copied at the segment's first block,
             // so nothing here waits for the load and no divergent control flow
-            // separates the scalar bookkeeping of the pipeline. A shared prefix
-            // (m requests) stacks them: row r is head r % G of request b + r / G.
-            const int hrow = row < mt.m * G ? row : 0;
-            int qb = mt.b, qh = hrow;
-            if (SRC == SRC_SHARED) {
-                const int mem = hrow / G;
-                qb += mem;
-                qh = hrow - mem * G;
-            }
-            const uint16_t *qp = a.q + ((size_t)qb * a.Hq + (size_t)mt.g * G + qh) * D;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int d0 = KVFP8 ? 16 * grp + 64 * (kk >> 1) + 8 * (kk & 1) : 32 * kk + 8 * grp;
-                s.q[kk] = *reinterpret_cast<const u32x4 *>(qp + d0);  // zeroed at use
-            }
-            if (KVFP8) {
-                if (SRC == SRC_SHARED) {   // per row: the scales of the row's request
-                    mt.ksc = a.k_scale[(size_t)qb * a.Hkv + mt.g];
-                    mt.vsc = a.v_scale[(size_t)qb * a.Hkv + mt.g];
-                } else {
-                    mt.ksc = ldc(a.k_scale, (size_t)mt.b * a.Hkv + mt.g);
-                    mt.vsc = ldc(a.v_scale, (size_t)mt.b * a.Hkv + mt.g);
-                }
-            }
+            // separates the scalar bookkeeping of the pipeline.
+            load_q(s.q, mt, 0, mt.ksc, mt.vsc);
         }
         // The slab address is wave-uniform (scalar registers); each lane adds its
         // fixed 32-bit offset, so the loads take the scalar-base form and no
@@ -700,25 +721,29 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
 
     // ---- end of a segment: merge the 4 waves and write ------------------
     auto finish = [&](const Meta &mt) {
-        const float l_tot = xsum4(l_run);
-        const float e_tot = xsum4(e_run);
         const int rows = mt.m * G;   // query rows of this segment
-        if (row < rows) {
-            if (grp == 0) {
-                lds.m[wave][row] = m_run;
-                lds.l[wave][row] = l_tot;
-                lds.e[wave][row] = e_tot;
-                if (SRC == SRC_SHARED && wave == 0)
-                    lds.vs[row] = vsc_run;   // per row: its request's V scale
-            }
 #pragma unroll
-            for (int mb = 0; mb < 8; ++mb) {
-                if (KVFP8) {
+        for (int cb = 0; cb < NCB; ++cb) {
+            const float l_tot = xsum4(l_run[cb]);
+            const float e_tot = xsum4(e_run[cb]);
+            const int rr = 16 * cb + row;
+            if (rr < rows) {
+                if (grp == 0) {
+                    lds.m[wave][rr] = m_run[cb];
+                    lds.l[wave][rr] = l_tot;
+                    lds.e[wave][rr] = e_tot;
+                    if (is_shared(SRC) && wave == 0)
+                        lds.vs[rr] = vsc_run[cb];   // per row: its request's V scale
+                }
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        lds.acc[wave][row][out_dim<1>(mb, 4 * grp + i)] = acc[mb][i];
-                } else {
-                    *reinterpret_cast<f32x4 *>(&lds.acc[wave][row][16 * mb + 4 * grp]) = acc[mb];
+                for (int mb = 0; mb < 8; ++mb) {
+                    if (KVFP8) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            lds.acc[wave][rr][out_dim<1>(mb, 4 * grp + i)] = acc[cb][mb][i];
+                    } else {
+                        *reinterpret_cast<f32x4 *>(&lds.acc[wave][rr][16 * mb + 4 * grp]) = acc[cb][mb];
+                    }
                 }
             }
         }
@@ -742,11 +767,11 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
                     const f32x4 x = *reinterpret_cast<const f32x4 *>(&lds.acc[v][h][d4]);
                     o += e * x;
                 }
-                const float r = (SRC == SRC_SHARED ? lds.vs[h] : vsc_run) / den;
+                const float r = (is_shared(SRC) ? lds.vs[h] : vsc_run[0]) / den;
                 o *= r;
                 lse2 = M + log2f(ex);
             }
-            const int mem = SRC == SRC_SHARED ? h / G : 0;   // row h: head h % G of request b + h / G
+            const int mem = is_shared(SRC) ? h / G : 0;   // row h: head h % G of request b + h / G
             const size_t hq = (size_t)(mt.b + mem) * a.Hq + (size_t)mt.g * G + (h - mem * G);
             const size_t prow = (size_t)mt.slot * a.slot_rows + h;   // partial row
             if (mt.direct) {
@@ -806,22 +831,36 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
         // K/V registers are consumed on every path (the math runs even for an
         // empty slice and then contributes nothing); q only at a segment's
         // first block, which is the only block that loads it.
+        // the second column block only when the segment's rows reach it
+        // (wave-uniform: a shared item of more than 16 query rows)
+        const bool two = NCB == 2 && mt.m * G > 16;
         if (mt.first) {
+            float ksc1 = 1.f, vsc1 = 1.f;
+            if (NCB == 2 && two)   // loaded here, once per segment (a memory round trip)
+                load_q(qreg[NCB - 1], mt, 1, ksc1, vsc1);
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                qreg[kk] = row < mt.m * G ? s.q[kk] : u32x4{0u, 0u, 0u, 0u};
-            m_run = -INFINITY;
-            l_run = 0.f;
-            e_run = 0.f;
+            for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-            sc = a.scale_log2 * mt.ksc;
-            vsc_run = mt.vsc;
+                for (int kk = 0; kk < 4; ++kk) {
+                    const u32x4 q = cb == 0 ? s.q[kk] : qreg[cb][kk];
+                    qreg[cb][kk] = (cb == 0 || two) && 16 * cb + row < mt.m * G ? q : u32x4{0u, 0u, 0u, 0u};
+                }
+                m_run[cb] = -INFINITY;
+                l_run[cb] = 0.f;
+                e_run[cb] = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    acc[cb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+                sc[cb] = a.scale_log2 * (cb == 0 ? mt.ksc : ksc1);
+                vsc_run[cb] = cb == 0 ? mt.vsc : vsc1;
+            }
         }
         {
-            // scores: S^T[token 4*grp+i][head row]
-            f32x4 st = {0.f, 0.f, 0.f, 0.f};
+            // scores: S^T[token 4*grp+i][head row], per column block
+            f32x4 st[NCB];
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+                st[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (KVFP8) {
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
@@ -832,49 +871,64 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
                     const bf16x2 c2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
                     const bf16x2 c3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
                     const bf16x8 kv = {c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
-                    st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, __builtin_bit_cast(bf16x8, qreg[kk]), st, 0, 0, 0);
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb)
+                        if (cb == 0 || two)
+                            st[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, __builtin_bit_cast(bf16x8, qreg[cb][kk]),
+                                                                             st[cb], 0, 0, 0);
                 }
             } else {
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, s.k[kk]),
-                                                                 __builtin_bit_cast(bf16x8, qreg[kk]), st, 0, 0, 0);
-            }
+                for (int cb = 0; cb < NCB; ++cb)
+                    if (cb == 0 || two) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                st[i] *= sc;
-            if (mt.nv < kSlice) {
+                        for (int kk = 0; kk < 4; ++kk)
+                            st[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, s.k[kk]),
+                                                                             __builtin_bit_cast(bf16x8, qreg[cb][kk]),
+                                                                             st[cb], 0, 0, 0);
+                    }
+            }
+            s16x4 pb[NCB];
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                if (!(cb == 0 || two))
+                    continue;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    st[i] = 4 * grp + i >= mt.nv ? -INFINITY : st[i];
-            }
-            float mx = fmaxf(fmaxf(st[0], st[1]), fmaxf(st[2], st[3]));
-            mx = xmax4(mx);
-            // Lazy rescaling: the reference maximum m_run only moves (and the
-            // running sums are rescaled) when a head's scores exceed it by more
-            // than kLazy (log2 units). Weights 2^(s - m_run) then stay <= 2^kLazy,
-            // exact in fp32 and bf16 alike, and every later step uses the same
-            // reference, so the result is unchanged while most slices skip the
-            // 34 multiplies of a rescale.
-            if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy) != 0) {
-                const float m_new = fmaxf(m_run, mx);
-                const float alpha = fast_exp2(m_run - m_new);
-                l_run *= alpha;
-                e_run *= alpha;
+                    st[cb][i] *= sc[cb];
+                if (mt.nv < kSlice) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    acc[i] *= alpha;
-                m_run = m_new;
-            }
-            const float m_use = m_run == -INFINITY ? 0.f : m_run;
-            f32x4 p;
+                    for (int i = 0; i < 4; ++i)
+                        st[cb][i] = 4 * grp + i >= mt.nv ? -INFINITY : st[cb][i];
+                }
+                float mx = fmaxf(fmaxf(st[cb][0], st[cb][1]), fmaxf(st[cb][2], st[cb][3]));
+                mx = xmax4(mx);
+                // Lazy rescaling: the reference maximum m_run only moves (and the
+                // running sums are rescaled) when a head's scores exceed it by more
+                // than kLazy (log2 units). Weights 2^(s - m_run) then stay <= 2^kLazy,
+                // exact in fp32 and bf16 alike, and every later step uses the same
+                // reference, so the result is unchanged while most slices skip the
+                // 34 multiplies of a rescale.
+                if (__builtin_amdgcn_ballot_w64(mx > m_run[cb] + kLazy) != 0) {
+                    const float m_new = fmaxf(m_run[cb], mx);
+                    const float alpha = fast_exp2(m_run[cb] - m_new);
+                    l_run[cb] *= alpha;
+                    e_run[cb] *= alpha;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                p[i] = fast_exp2(st[i] - m_use);
-            const s16x4 pb = pack_bf16x4(p);
-            const f32x4 pr = unpack_bf16x4(pb);
-            l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-            e_run += (p[0] + p[1]) + (p[2] + p[3]);
+                    for (int i = 0; i < 8; ++i)
+                        acc[cb][i] *= alpha;
+                    m_run[cb] = m_new;
+                }
+                const float m_use = m_run[cb] == -INFINITY ? 0.f : m_run[cb];
+                f32x4 p;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    p[i] = fast_exp2(st[cb][i] - m_use);
+                pb[cb] = pack_bf16x4(p);
+                const f32x4 pr = unpack_bf16x4(pb[cb]);
+                l_run[cb] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+                e_run[cb] += (p[0] + p[1]) + (p[2] + p[3]);
+            }
             // rows past the length may hold anything (NaN): zero them
             if (mt.nv < kSlice && row >= mt.nv) {
 #pragma unroll
@@ -895,8 +949,12 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
                         t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, s.v[kk]),
                                                                     sel16[ss], zero, 0, 0, 0);
                     }
-                    acc[2 * kk + ss] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pack_bf16x4(t), pb, acc[2 * kk + ss],
-                                                                                 0, 0, 0);
+                    const s16x4 vt = pack_bf16x4(t);
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb)
+                        if (cb == 0 || two)
+                            acc[cb][2 * kk + ss] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pb[cb],
+                                                                                             acc[cb][2 * kk + ss], 0, 0, 0);
                 }
             }
         }
@@ -997,6 +1055,8 @@ hipError_t launch_decode(const DecodeArgs &a, int src, int kv_fp8, int grid, hip
     case 7: VLKV_LAUNCH(SRC_FUSED_STATIC, 1); break;
     case 8: VLKV_LAUNCH(SRC_SHARED, 0); break;
     case 9: VLKV_LAUNCH(SRC_SHARED, 1); break;
+    case 10: VLKV_LAUNCH(SRC_SHARED_WIDE, 0); break;
+    case 11: VLKV_LAUNCH(SRC_SHARED_WIDE, 1); break;
     default: return hipErrorInvalidValue;
     }
 #undef VLKV_LAUNCH

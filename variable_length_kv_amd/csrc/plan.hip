@@ -19,9 +19,9 @@
 //
 //   shared  (mode 2) requests whose page tables begin with the same valid
 //           pages are grouped (runs of adjacent sharers cut into groups of
-//           R = 16 / G); a group reads its common prefix once as one "item"
-//           whose query rows are the members' heads, and each request keeps
-//           an item for the rest of its tokens. The partition above then runs
+//           R = 32 / G for G >= 8, 16 / G below); a group reads its common
+//           prefix once as one "item" whose query rows are the members'
+//           heads, and each request keeps an item for the rest of its tokens. The partition above then runs
 //           over (item, g, t) units. Prefix caching is on the article's list
 //           of situations the kernels must handle [same page, same section,
 //           production-reliability paragraph].

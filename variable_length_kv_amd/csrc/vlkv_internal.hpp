@@ -26,8 +26,11 @@ enum : int { H_ITEMS = 4, H_GROUP = 5 };
 // plan modes (the public ATTN_DYNAMIC / ATTN_STATIC / ATTN_SHARED)
 enum : int { MODE_DYNAMIC = 0, MODE_STATIC = 1, MODE_SHARED = 2 };
 
-// Requests per shared pass: one MFMA column block holds kMaxGroup query rows.
-__host__ __device__ constexpr int shared_group(int G) { return G >= kMaxGroup ? 1 : kMaxGroup / G; }
+// Requests per shared pass: the shared decode stacks them in MFMA column
+// blocks of kMaxGroup query rows, two blocks when one holds two requests or
+// fewer (G >= 8), else one (G <= kMaxGroup).
+__host__ __device__ constexpr int shared_blocks(int G) { return G >= 8 ? 2 : 1; }
+__host__ __device__ constexpr int shared_group(int G) { return shared_blocks(G) * kMaxGroup / G; }
 
 // Byte offsets of the workspace regions (all 256-B aligned). In mode 2 the
 // plan is over items (at most 2B): len_eff, tiles_prefix, seg_prefix, first_wg
@@ -47,7 +50,10 @@ enum PlanSrc : int {
     SRC_FUSED_DYNAMIC = 2,  // single launch: each workgroup derives its range from the lengths
     SRC_FUSED_STATIC = 3,   // single launch, static split-K
     SRC_SHARED = 4,         // plan arrays written by attn_plan (mode 2: items, prefix-shared pages)
+    SRC_SHARED_WIDE = 5,    // the same with two MFMA column blocks of query rows (G >= 8)
 };
+
+__host__ __device__ constexpr bool is_shared(int src) { return src == SRC_SHARED || src == SRC_SHARED_WIDE; }
 
 struct Shape {
     int B, Hq, Hkv, G, D, P, num_pages, pt_stride, T, W, kv_fp8, mode, S;
