@@ -57,6 +57,25 @@ constexpr int kMergeBatch = 4;         // partials folded together by the LSE me
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Wave priority from a workgroup's progress through its blocks: 3 for the
+// first half, 2 up to 80%, 1 up to 95%, 0 for the rest. Two workgroups share a
+// CU, and among ready waves of equal priority the SIMD issues the older one
+// first, so the workgroup dispatched second falls behind and finishes last,
+// alone on its CU. With priorities that fall as the work progresses, the
+// workgroup that is behind issues first whenever both are ready.
+__device__ __forceinline__ void set_progress_priority(int done, int total)
+{
+    const int64_t d = done, t = total;   // compares only: no division in the loop
+    if (2 * d < t)
+        __builtin_amdgcn_s_setprio(3);
+    else if (5 * d < 4 * t)
+        __builtin_amdgcn_s_setprio(2);
+    else if (20 * d < 19 * t)
+        __builtin_amdgcn_s_setprio(1);
+    else
+        __builtin_amdgcn_s_setprio(0);
+}
+
 // Read-only data of the step (plan arrays, lengths, page table, scales) is read
 // through the constant address space: wave-uniform addresses then become scalar
 // loads, which are counted apart from the K/V vector loads, so waiting for a
@@ -973,6 +992,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
     for (int i = 0; i < kSlots; ++i)
         issue(sl[i], mt[i]);
     for (int it = 0; it < nblk; it += kSlots) {
+        set_progress_priority(it, nblk);
 #pragma unroll
         for (int i = 0; i < kSlots; ++i) {
             compute(sl[i], mt[i]);
