@@ -14,7 +14,8 @@ merit is effective KV bandwidth: every cached K and V row of the batch once
 Also reported (field "extra"): the skewed batch (1 x 16000 + 63 x 1000 tokens)
 under the dynamic plan and under the in-library static split-K at its default
 split count and a split sweep, the long-tail batch, and the 256-step
-continuous-batching trace over an fp8 e4m3 cache (plan rebuilt every step).
+continuous-batching trace over an fp8 e4m3 cache (plan rebuilt every step;
+the single-launch step also captured once in a HIP graph and replayed).
 Those are timed per step with HIP events, with a 1 GiB read sweep between steps
 so that no step starts with the previous step's data in the 256 MB Infinity
 Cache. The CPU reference is timed on the host as a reported baseline
@@ -425,15 +426,32 @@ def trace_leg(torch, L, W_of, flush, steps=256):
         fused()
         three([ev(torch) for _ in range(4)])
     torch.cuda.synchronize()
-    tf, t3, kvb = [], [], []
+    # the single-launch step captured once in a HIP graph; every step's inputs
+    # are written in place into the same buffers, so one graph serves them all
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fused()
+    torch.cuda.synchronize()
+    tf, t3, tg, kvb, host_eager, host_graph = [], [], [], [], [], []
     while True:
         flush.sum()
         a, b = ev(torch), ev(torch)
         a.record()
+        h0 = time.perf_counter()
         fused()
+        host_eager.append(time.perf_counter() - h0)
         b.record()
         torch.cuda.synchronize()
         tf.append(a.elapsed_time(b))
+        flush.sum()
+        a, b = ev(torch), ev(torch)
+        a.record()
+        h0 = time.perf_counter()
+        graph.replay()
+        host_graph.append(time.perf_counter() - h0)
+        b.record()
+        torch.cuda.synchronize()
+        tg.append(a.elapsed_time(b))
         flush.sum()
         evs = [ev(torch) for _ in range(4)]
         three(evs)
@@ -446,6 +464,7 @@ def trace_leg(torch, L, W_of, flush, steps=256):
     torch.cuda.synchronize()
     ta = np.array([a.elapsed_time(b) for a, b in append_ev]) * 1e3   # us, steps 1..
     tf = np.array(tf) * 1e3   # us
+    tg = np.array(tg) * 1e3
     t3 = np.array(t3) * 1e3
     t3s = t3.sum(axis=1)
     kvb = np.array(kvb, np.float64)
@@ -461,6 +480,9 @@ def trace_leg(torch, L, W_of, flush, steps=256):
 
     out_d = {"steps": steps, "num_wgs": W, "kv_gb_mean": round(float(kvb.mean()) / 1e9, 4),
              "single_launch": summary(tf),
+             "single_launch_graph_replay": summary(tg),
+             "host_issue_us_median": {"single_launch_eager": round(float(np.median(host_eager)) * 1e6, 2),
+                                      "graph_replay": round(float(np.median(host_graph)) * 1e6, 2)},
              "three_launch": summary(t3s)}
     with_append = tf[1:] + ta
     out_d["append_us_median"] = round(float(np.median(ta)), 2)
