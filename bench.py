@@ -11,7 +11,8 @@ steps run back to back between two device synchronisations. The figure of
 merit is effective KV bandwidth: every cached K and V row of the batch once
 (2 * Hkv * D * 2 bytes per token) divided by the step time.
 
-Also reported (field "extra"): the skewed batch (1 x 16000 + 63 x 1000 tokens)
+Also reported (field "extra"): the tiny batch (4 requests, launch-bound), the
+skewed batch (1 x 16000 + 63 x 1000 tokens)
 under the dynamic plan and under the in-library static split-K at its default
 split count and a split sweep, the long-tail batch, and the 256-step
 continuous-batching trace over an fp8 e4m3 cache (plan rebuilt every step;
@@ -295,6 +296,24 @@ def batch_leg(cid, torch, L, wl, W_of, flush, static_sweep=False):
     return entry
 
 
+def tiny_leg(torch, L, wl, W_of, steps=200):
+    """Workload 0: 4 requests of {17, 64, 200, 1000} tokens, 8 query heads on
+    one kv head, 16-token pages. It moves 0.66 MB of KV, so a step is bound by
+    launch latency, not by HBM. Steps are queued behind a spin kernel so that
+    the events see the GPU's time per step rather than the host's time to issue
+    it."""
+    c = wl.config_case(0)
+    W = W_of(c.lengths, c.Hkv)
+    r = Runner(c, torch, L, W)
+    a = r.attention(L.ATTN_DYNAMIC)
+    fused = bracketed_ahead(lambda: r.fused(a), steps, torch)
+    three = bracketed_ahead(lambda: r.three(a), steps, torch)
+    del a, r
+    return {"kv_mb": round(c.kv_bytes / 1e6, 3), "tokens": c.total_tokens, "num_wgs": W,
+            "single_launch_us_per_step": us(fused), "three_launch_us_per_step": us(three),
+            "single_launch_gbs": round(c.kv_bytes / (fused * 1e-3) / 1e9, 1)}
+
+
 def shared_leg(torch, L, wl, W_of, flush, Hq):
     """Workload 5: prefix caching. 16 groups of 4 requests share an 8192-token
     prompt (its 128 pages aliased in their page tables), each request with its
@@ -567,8 +586,8 @@ def main():
     ap.add_argument("--wgs-per-cu", type=int, default=0,
                     help="workgroups per CU of the dynamic plan (0: the library's suggestion per workload)")
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
-    ap.add_argument("--extra-legs", default="skewed,long_tail,trace,shared,router",
-                    help="comma list of the extra workloads to run (skewed, long_tail, trace, shared, router)")
+    ap.add_argument("--extra-legs", default="tiny,skewed,long_tail,trace,shared,router",
+                    help="comma list of the extra workloads to run (tiny, skewed, long_tail, trace, shared, router)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--trace-steps", type=int, default=256)
     ap.add_argument("--traffic-probe", action="store_true",
@@ -653,6 +672,9 @@ def main():
         extra = {}
         legs = set(args.extra_legs.split(","))
         flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+        if "tiny" in legs:
+            extra["tiny"] = tiny_leg(torch, L, wl, W_of)
+            log(f"bench: tiny: {json.dumps(extra['tiny'])}")
         if "skewed" in legs:
             extra["skewed"] = batch_leg(2, torch, L, wl, W_of, flush, static_sweep=True)
             log(f"bench: skewed: {json.dumps(extra['skewed'])}")
