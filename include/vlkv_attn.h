@@ -143,7 +143,12 @@ int attn_device_cu_count(int device, int32_t *cus);
  * remaining tokens. The partition above then
  * runs over (item, kv head, tile) units. Results equal the other modes' up to
  * the order of the softmax merge. The plan's arrays are over items
- * (attn_read_plan, attn_read_plan_items).
+ * (attn_read_plan, attn_read_plan_items). Batches whose page tables alias
+ * pages should use this mode: the other modes stream K/V with non-temporal
+ * loads, so a page that several requests read in one step is fetched from
+ * memory each time.
+ * Note: "non-temporal" above is a cache policy of the loads only; it does not
+ * change any result.
  * The workspace contents stay valid until the next attn_plan on it.
  */
 int attn_plan(const attn_shape *shape, const int32_t *lengths, const int32_t *page_table,

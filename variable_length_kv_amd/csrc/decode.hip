@@ -17,12 +17,20 @@
 // four states are merged through LDS at the end of each segment.
 //
 // Per wave and slice (16 tokens x 128 dims of K and of V):
-//   * K and V rows are loaded with 16-byte loads straight into MFMA operand
-//     registers: lane l holds token row l%16 and a run of dims selected by
-//     l/16. For bf16 each load instruction reads 64 contiguous bytes of 16 rows
-//     and four instructions read the slice once; for fp8 two instructions do.
-//     Two slices per wave are in flight (register double buffering) on top of
-//     several resident waves per SIMD; no LDS staging is needed for K or V.
+//   * The slice's K and V rows (4 KB each for bf16, 2 KB for fp8, contiguous
+//     in the page) are read with 16-byte non-temporal loads, lane l taking
+//     bytes 16 l + 1024 i of load i: each load instruction reads 1 KB of whole
+//     128-byte lines, and the lines are not kept in the caches (every K/V byte
+//     is read once per step). Two slices per wave are in flight in registers
+//     on top of two resident waves per SIMD.
+//   * At the slice's compute the wave writes its registers to its own LDS
+//     staging rows and reads back the MFMA operand layout: lane l holds token
+//     row l%16 and a run of dims selected by l/16. Loading that layout straight
+//     from memory reads 64 bytes of each of 16 rows per instruction, half
+//     lines that a non-temporal load would fetch twice; through LDS the loads
+//     stream at the rate of contiguous reads. (The two-column-block variant
+//     for prefix-shared items keeps the direct operand loads: staging would
+//     cost it the registers and LDS of its second block.)
 //   * S^T = K Q^T with 4 bf16 MFMAs 16x16x32 (16 tokens x 16 heads; heads >= G
 //     are zero). fp8 K codes are widened to bf16 exactly first. The result's
 //     lane layout (lane l: tokens 4*(l/16)+i, head l%16) is exactly the B
@@ -52,6 +60,7 @@ typedef short s16x4 __attribute__((__vector_size__(4 * sizeof(short))));
 
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kLdsRow = kHeadDim + 4;  // padded fp32 row of the merge buffer
+constexpr int kStgRow = kHeadDim * 2 + 16;  // padded byte row of a staged K or V slice
 constexpr float kLazy = 8.f;           // lazy-rescale threshold (log2 units)
 constexpr int kMergeBatch = 4;         // partials folded together by the LSE merge
 
@@ -509,8 +518,12 @@ __device__ __forceinline__ void merge_partials(const float *part_o, const float 
 
 template <int NCB>
 struct DecodeLds {
+    static constexpr bool kStage = NCB == 1;   // K/V restaged through LDS (one column block)
     union {
-        float acc[kWaves][kMaxGroup * NCB][kLdsRow];  // per-wave states at a segment's end
+        struct {
+            float acc[kWaves][kMaxGroup * NCB][kLdsRow];  // per-wave states at a segment's end
+            uint8_t stg[kWaves][2][kStage ? 16 * kStgRow : 16];   // per-wave K and V slice staging
+        };
         struct {
             int32_t tp[kMaxBatch + 1];          // single launch: tiles prefix (prologue only)
             int32_t len[kMaxBatch];             // and validated lengths
@@ -540,6 +553,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
     // 32 / G requests' heads in two blocks that read each K/V slice once.
     constexpr int NCB = SRC == SRC_SHARED_WIDE ? 2 : 1;
     __shared__ __attribute__((aligned(16))) DecodeLds<NCB> lds;
+    constexpr bool kStage = DecodeLds<NCB>::kStage;
 
     const int G = a.G;
     constexpr int D = kHeadDim;
@@ -725,16 +739,30 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
         if (KVFP8) {
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
-                s.k[p] = *reinterpret_cast<const u32x4 *>(kp + lane_off + 64 * p);
-                s.v[p] = *reinterpret_cast<const u32x4 *>(vp + lane_off + 64 * p);
+                if constexpr (kStage) {
+                    s.k[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kp + 1024 * p + 16 * lane));
+                    s.v[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vp + 1024 * p + 16 * lane));
+                } else {
+                    s.k[p] = *reinterpret_cast<const u32x4 *>(kp + lane_off + 64 * p);
+                    s.v[p] = *reinterpret_cast<const u32x4 *>(vp + lane_off + 64 * p);
+                }
             }
         } else {
+            if constexpr (kStage) {
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                s.k[kk] = *reinterpret_cast<const u32x4 *>(kp + lane_off + 64 * kk);
+                for (int kk = 0; kk < 4; ++kk)
+                    s.k[kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kp + 1024 * kk + 16 * lane));
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                s.v[kk] = *reinterpret_cast<const u32x4 *>(vp + lane_off + 64 * kk);
+                for (int kk = 0; kk < 4; ++kk)
+                    s.v[kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vp + 1024 * kk + 16 * lane));
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    s.k[kk] = *reinterpret_cast<const u32x4 *>(kp + lane_off + 64 * kk);
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    s.v[kk] = *reinterpret_cast<const u32x4 *>(vp + lane_off + 64 * kk);
+            }
         }
     };
 
@@ -847,6 +875,30 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
 
     // ---- math of one block ----------------------------------------------
     auto compute = [&](Slot &s, const Meta &mt) {
+        if constexpr (kStage) {
+            // Load i of lane l brought slice bytes [1024 i + 16 l, +16): row
+            // (1024 i + 16 l) / RB, column byte (1024 i + 16 l) % RB, RB = D * EB.
+            // Write them to this wave's staging rows, then read back the operand
+            // layout (row = lane % 16, bytes 64 i + 16 * (lane / 16)). LDS
+            // operations of one wave complete in order, so no barrier is needed.
+            constexpr int RB = D * EB;
+            constexpr int NL = KVFP8 ? 2 : 4;
+            uint8_t *sk = lds.stg[wave][0];
+            uint8_t *sv = lds.stg[wave][1];
+#pragma unroll
+            for (int i = 0; i < NL; ++i) {
+                const int byte = 1024 * i + 16 * lane;
+                const int o = (byte / RB) * kStgRow + byte % RB;
+                *reinterpret_cast<u32x4 *>(sk + o) = s.k[i];
+                *reinterpret_cast<u32x4 *>(sv + o) = s.v[i];
+            }
+#pragma unroll
+            for (int i = 0; i < NL; ++i) {
+                const int o = row * kStgRow + 64 * i + 16 * grp;
+                s.k[i] = *reinterpret_cast<const u32x4 *>(sk + o);
+                s.v[i] = *reinterpret_cast<const u32x4 *>(sv + o);
+            }
+        }
         // K/V registers are consumed on every path (the math runs even for an
         // empty slice and then contributes nothing); q only at a segment's
         // first block, which is the only block that loads it.
