@@ -28,9 +28,9 @@
 //     row l%16 and a run of dims selected by l/16. Loading that layout straight
 //     from memory reads 64 bytes of each of 16 rows per instruction, half
 //     lines that a non-temporal load would fetch twice; through LDS the loads
-//     stream at the rate of contiguous reads. (The two-column-block variant
-//     for prefix-shared items keeps the direct operand loads: staging would
-//     cost it the registers and LDS of its second block.)
+//     stream at the rate of contiguous reads. The staging rows share LDS with
+//     the segment-end merge buffer; a barrier before each merge separates the
+//     two uses.
 //   * S^T = K Q^T with 4 bf16 MFMAs 16x16x32 (16 tokens x 16 heads; heads >= G
 //     are zero). fp8 K codes are widened to bf16 exactly first. The result's
 //     lane layout (lane l: tokens 4*(l/16)+i, head l%16) is exactly the B
@@ -518,12 +518,9 @@ __device__ __forceinline__ void merge_partials(const float *part_o, const float 
 
 template <int NCB>
 struct DecodeLds {
-    static constexpr bool kStage = NCB == 1;   // K/V restaged through LDS (one column block)
     union {
-        struct {
-            float acc[kWaves][kMaxGroup * NCB][kLdsRow];  // per-wave states at a segment's end
-            uint8_t stg[kWaves][2][kStage ? 16 * kStgRow : 16];   // per-wave K and V slice staging
-        };
+        float acc[kWaves][kMaxGroup * NCB][kLdsRow];  // per-wave states at a segment's end
+        uint8_t stg[kWaves][2][16 * kStgRow];          // per-wave K and V slice staging (during blocks)
         struct {
             int32_t tp[kMaxBatch + 1];          // single launch: tiles prefix (prologue only)
             int32_t len[kMaxBatch];             // and validated lengths
@@ -553,7 +550,6 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
     // 32 / G requests' heads in two blocks that read each K/V slice once.
     constexpr int NCB = SRC == SRC_SHARED_WIDE ? 2 : 1;
     __shared__ __attribute__((aligned(16))) DecodeLds<NCB> lds;
-    constexpr bool kStage = DecodeLds<NCB>::kStage;
 
     const int G = a.G;
     constexpr int D = kHeadDim;
@@ -672,8 +668,6 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
     }
 
     int bad_page = 0;
-    // this lane's byte offset inside a 16-row slice: row (token) and 16-byte column group
-    const uint32_t lane_off = (uint32_t)row * (D * EB) + 16u * grp;
 
     // ---- loads of one block into a slot ---------------------------------
     // K/V loads are issued for every slot, also past the end of the work or
@@ -719,8 +713,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
             load_q(s.q, mt, 0, mt.ksc, mt.vsc);
         }
         // The slab address is wave-uniform (scalar registers); each lane adds its
-        // fixed 32-bit offset, so the loads take the scalar-base form and no
-        // 64-bit address arithmetic runs per lane.
+        // fixed 32-bit offset (16 bytes per lane, 1 KB per load), so the loads
+        // take the scalar-base form and no 64-bit address arithmetic runs per lane.
         size_t slab = (size_t)mt.g * page_head_bytes;   // page 0 of kv head g
         if (mt.valid && mt.nv > 0) {
             const int tok = mt.tbase + mt.tok0;   // token index in the request
@@ -739,36 +733,23 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
         if (KVFP8) {
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
-                if constexpr (kStage) {
-                    s.k[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kp + 1024 * p + 16 * lane));
-                    s.v[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vp + 1024 * p + 16 * lane));
-                } else {
-                    s.k[p] = *reinterpret_cast<const u32x4 *>(kp + lane_off + 64 * p);
-                    s.v[p] = *reinterpret_cast<const u32x4 *>(vp + lane_off + 64 * p);
-                }
+                s.k[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kp + 1024 * p + 16 * lane));
+                s.v[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vp + 1024 * p + 16 * lane));
             }
         } else {
-            if constexpr (kStage) {
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    s.k[kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kp + 1024 * kk + 16 * lane));
+            for (int kk = 0; kk < 4; ++kk)
+                s.k[kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kp + 1024 * kk + 16 * lane));
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    s.v[kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vp + 1024 * kk + 16 * lane));
-            } else {
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    s.k[kk] = *reinterpret_cast<const u32x4 *>(kp + lane_off + 64 * kk);
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    s.v[kk] = *reinterpret_cast<const u32x4 *>(vp + lane_off + 64 * kk);
-            }
+            for (int kk = 0; kk < 4; ++kk)
+                s.v[kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vp + 1024 * kk + 16 * lane));
         }
     };
 
     // ---- end of a segment: merge the 4 waves and write ------------------
     auto finish = [&](const Meta &mt) {
         const int rows = mt.m * G;   // query rows of this segment
+        __syncthreads();   // every wave is done with its staging rows, which alias lds.acc
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
             const float l_tot = xsum4(l_run[cb]);
@@ -875,7 +856,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
 
     // ---- math of one block ----------------------------------------------
     auto compute = [&](Slot &s, const Meta &mt) {
-        if constexpr (kStage) {
+        {
             // Load i of lane l brought slice bytes [1024 i + 16 l, +16): row
             // (1024 i + 16 l) / RB, column byte (1024 i + 16 l) % RB, RB = D * EB.
             // Write them to this wave's staging rows, then read back the operand
