@@ -9,7 +9,8 @@
 // workgroup's sequence of (request, kv head, block range) segments comes from:
 // the plan arrays attn_plan wrote, or (single launch) the lengths themselves,
 // from which every workgroup derives its own unit range; then the last
-// workgroup to finish a split (request, kv head) pair merges its partials.
+// workgroup to finish a split (request, kv head) pair merges its partials,
+// after its own blocks.
 //
 // Workgroup = 4 wave64s. A 64-token block of one (request b, kv head g) is split
 // into four 16-token slices, one per wave; every wave walks the same sequence of
@@ -530,7 +531,10 @@ struct DecodeLds {
     float l[kWaves][kMaxGroup * NCB];
     float e[kWaves][kMaxGroup * NCB];
     int red[2 * kWaves];
-    int flag;
+    // single launch: the split pairs this workgroup arrived at last, merged
+    // after its block loop (at most two: only a first and a last segment split)
+    int npend;
+    int pend[2][5];   // b, g, nseg, wfirst, first_off
     float vs[kMaxGroup * NCB];   // SRC_SHARED: V scale of each query row
 };
 
@@ -668,6 +672,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
     }
 
     int bad_page = 0;
+    if (kFused && threadIdx.x == 0)
+        lds.npend = 0;   // read after the barriers of the first segment end
 
     // ---- loads of one block into a slot ---------------------------------
     // K/V loads are issued for every slot, also past the end of the work or
@@ -823,31 +829,25 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
         if (kFused && !mt.direct) {
             // Arrival: each wave waits for its coherent partial stores to
             // complete before the barrier, so they are visible device-wide before
-            // the counter moves; the last of the pair's nseg workgroups merges
-            // the pair's partials with coherent loads.
+            // the counter moves. The last of the pair's nseg workgroups resets
+            // the counter and notes the pair; it merges the pair's partials with
+            // coherent loads once its own blocks are done (kept out of the block
+            // loop, the merge code no longer crowds the loop's scalar registers).
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             const int bg = mt.b * a.Hkv + mt.g;
             if (tid == 0) {
                 const int old = __hip_atomic_fetch_add(a.counters + bg, 1, __ATOMIC_RELAXED,
                                                        __HIP_MEMORY_SCOPE_AGENT);
-                const int last = old == mt.nseg - 1;
-                if (last)   // every arrival of this step is in: leave the counter at 0
+                if (old == mt.nseg - 1) {   // every arrival of this step is in: leave the counter at 0
                     __hip_atomic_store(a.counters + bg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                lds.flag = last;
-            }
-            __syncthreads();
-            if (lds.flag) {
-                const int sr = a.slot_rows;
-                if (SRC == SRC_FUSED_DYNAMIC) {
-                    const int wf = mt.wfirst, off = mt.first_off;
-                    merge_partials<true>(a.part_o, a.part_lse, mt.nseg,
-                                         [=](int s) { return (2 * (wf + s) + (s == 0 ? off : 0)) * sr; },
-                                         G, a.Hq, mt.b, mt.g, a.out, a.lse);
-                } else {
-                    const int s0 = bg * a.S;
-                    merge_partials<true>(a.part_o, a.part_lse, mt.nseg, [=](int s) { return (s0 + s) * sr; },
-                                         G, a.Hq, mt.b, mt.g, a.out, a.lse);
+                    const int k = lds.npend;
+                    lds.pend[k][0] = mt.b;
+                    lds.pend[k][1] = mt.g;
+                    lds.pend[k][2] = mt.nseg;
+                    lds.pend[k][3] = mt.wfirst;
+                    lds.pend[k][4] = mt.first_off;
+                    lds.npend = k + 1;
                 }
             }
         }
@@ -1030,6 +1030,29 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
         for (int i = 0; i < kSlots; ++i) {
             compute(sl[i], mt[i]);
             issue(sl[i], mt[i]);
+        }
+    }
+
+    // single launch: merge the pairs this workgroup arrived at last
+    if (kFused) {
+        __syncthreads();
+        const int np = __builtin_amdgcn_readfirstlane(lds.npend);
+        for (int k = 0; k < np; ++k) {
+            const int pb = __builtin_amdgcn_readfirstlane(lds.pend[k][0]);
+            const int pg = __builtin_amdgcn_readfirstlane(lds.pend[k][1]);
+            const int pn = __builtin_amdgcn_readfirstlane(lds.pend[k][2]);
+            const int wf = __builtin_amdgcn_readfirstlane(lds.pend[k][3]);
+            const int off = __builtin_amdgcn_readfirstlane(lds.pend[k][4]);
+            const int sr = a.slot_rows;
+            if (SRC == SRC_FUSED_DYNAMIC) {
+                merge_partials<true>(a.part_o, a.part_lse, pn,
+                                     [=](int s) { return (2 * (wf + s) + (s == 0 ? off : 0)) * sr; }, G, a.Hq,
+                                     pb, pg, a.out, a.lse);
+            } else {
+                const int s0 = (pb * a.Hkv + pg) * a.S;
+                merge_partials<true>(a.part_o, a.part_lse, pn, [=](int s) { return (s0 + s) * sr; }, G, a.Hq, pb,
+                                     pg, a.out, a.lse);
+            }
         }
     }
 
