@@ -842,12 +842,14 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
                 if (old == mt.nseg - 1) {   // every arrival of this step is in: leave the counter at 0
                     __hip_atomic_store(a.counters + bg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     const int k = lds.npend;
-                    lds.pend[k][0] = mt.b;
-                    lds.pend[k][1] = mt.g;
-                    lds.pend[k][2] = mt.nseg;
-                    lds.pend[k][3] = mt.wfirst;
-                    lds.pend[k][4] = mt.first_off;
-                    lds.npend = k + 1;
+                    if (k < 2) {   // a contiguous unit range splits at most its first and last pair
+                        lds.pend[k][0] = mt.b;
+                        lds.pend[k][1] = mt.g;
+                        lds.pend[k][2] = mt.nseg;
+                        lds.pend[k][3] = mt.wfirst;
+                        lds.pend[k][4] = mt.first_off;
+                        lds.npend = k + 1;
+                    }
                 }
             }
         }
