@@ -112,6 +112,13 @@ def test_dynamic_plan_against_enumeration(seed):
         ws = sorted(segs.get(bg, ()))
         assert ws == list(range(ws[0], ws[-1] + 1)) if ws else True  # one run per workgroup span
     assert p["seg_prefix"].tolist() == expect_prefix
+    # a workgroup shares at most two pairs with other workgroups: those of its
+    # first and last units (the single launch's merge list holds two entries)
+    for w in range(We):
+        split = {bg for bg, ws in segs.items() if len(ws) > 1 and w in ws}
+        lo, hi = p["wg_begin"][w], p["wg_begin"][w + 1]
+        ends = {units[lo][0] * Hkv + units[lo][1], units[hi - 1][0] * Hkv + units[hi - 1][1]}
+        assert split <= ends
     for w in range(W):
         if w < We:
             assert units[p["wg_begin"][w]][0] == p["wg_start_b"][w]
