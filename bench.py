@@ -6,8 +6,9 @@ Headline workload: 32 requests with context lengths uniform in [1000, 16000],
 random page table. A step is one decode step over the whole batch: the tile
 plan for the current lengths, the split-KV decode and the log-sum-exp merge.
 The headline step is attn_step (all three in one kernel launch); the
-three-launch form (attn_plan + attn_decode + attn_combine) is timed too. K
-steps run back to back between two device synchronisations. The figure of
+three-launch form (attn_plan + attn_decode + attn_combine) is timed too. After
+--settle-s seconds of untimed steps (GPU clocks out of idle) and W warm-up
+steps, K steps run back to back between two device synchronisations. The figure of
 merit is effective KV bandwidth: every cached K and V row of the batch once
 (2 * Hkv * D * 2 bytes per token) divided by the step time.
 
@@ -160,6 +161,22 @@ def timed_three(run, att, steps, warmup, torch):
     torch.cuda.synchronize()
     per = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs])
     return ms, per
+
+
+def settle(run, att, torch, seconds):
+    """Untimed single-launch and three-launch steps for `seconds` of wall time
+    before anything is measured, so that the GPU clocks have left their idle
+    state: with only the W warm-up steps (a few ms) the first measurement of a
+    process reads a few per cent slow."""
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(25):
+            run.fused(att)
+            run.three(att)
+        torch.cuda.synchronize()
+        n += 25
+    return n
 
 
 def timed_fused(run, att, steps, warmup, torch):
@@ -589,6 +606,8 @@ def main():
     ap.add_argument("--extra-legs", default="tiny,skewed,long_tail,trace,shared,router",
                     help="comma list of the extra workloads to run (tiny, skewed, long_tail, trace, shared, router)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--settle-s", type=float, default=0.5,
+                    help="seconds of untimed steps before the first measurement (GPU clocks leave idle)")
     ap.add_argument("--trace-steps", type=int, default=256)
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only the launches that the rocprofv3 --pmc runs measure")
@@ -625,6 +644,8 @@ def main():
     W = W_of(c1.lengths, c1.Hkv)
     r1 = Runner(c1, torch, L, W)
     att = r1.attention(L.ATTN_DYNAMIC)
+    n_settle = settle(r1, att, torch, args.settle_s)
+    log(f"bench: {n_settle} untimed settling steps of each form ({args.settle_s} s)")
     ms, per_f = timed_fused(r1, att, args.steps, args.warmup, torch)
     ms3, per3 = timed_three(r1, att, args.steps, args.warmup, torch)
     launch_ms = float(per_f.mean())
@@ -652,7 +673,7 @@ def main():
                                "64 q / 8 kv heads, head_dim 128, bf16 KV, page 64, random page table",
                    "global_batch": c1.B, "seq_len": int(c1.lengths.max()), "parallelism": "single GPU",
                    "step": "attn_step: tile plan + split-KV decode + LSE merge in one launch",
-                   "tile_tokens": 64, "num_wgs": W, "us_per_step": us(ms),
+                   "tile_tokens": 64, "num_wgs": W, "settle_s": args.settle_s, "us_per_step": us(ms),
                    "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
                    "three_launch": {"us_per_step": us(ms3),
                                     "pct_hbm_peak": round(100 * kv / (ms3 * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
