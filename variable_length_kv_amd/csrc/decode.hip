@@ -64,6 +64,11 @@ constexpr int kLdsRow = kHeadDim + 4;  // padded fp32 row of the merge buffer
 constexpr int kStgRow = kHeadDim * 2 + 16;  // padded byte row of a staged K or V slice
 constexpr float kLazy = 8.f;           // lazy-rescale threshold (log2 units)
 constexpr int kMergeBatch = 4;         // partials folded together by the LSE merge
+// Word 3 of a raw buffer descriptor (gfx9 family): 32-bit data format, no
+// swizzle, no index. A data format of 0 would make every access read zero.
+constexpr int kRsrcWord3 = 0x00020000;
+// Cache policy of the K/V loads: non-temporal (every K/V byte is read once per step).
+constexpr int kLoadNT = 2;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -421,18 +426,13 @@ struct Walker {
     }
 };
 
-// Loads and stores of the partials exchanged between workgroups inside one
-// launch. Relaxed atomics at agent scope are coherent across the chip's L2
-// caches (they are performed at the device's coherence point), so no L2-wide
-// writeback or invalidation is needed; ordering comes from waiting for the
-// stores to complete before the arrival counter moves.
+// Stores of the partials exchanged between workgroups inside one launch:
+// relaxed atomic stores at agent scope, which the chip makes coherent across
+// its XCDs' L2 caches by writing them through to the device's coherence
+// point (the readers' side is the acquire fence before the merge).
 __device__ __forceinline__ void store_coherent(float *p, float x)
 {
     __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_coherent(const float *p)
-{
-    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The LSE merge of partial results (o normalised, lse in base 2) of one
@@ -486,14 +486,11 @@ __device__ __forceinline__ void merge_write(float M, float den, f32x4 o, uint16_
 // Merge n partials of one (request, kv head) pair into the bf16 output and the
 // natural-log lse. base_of(s) is the partial row of head 0 of the s-th partial
 // (its heads are the G rows from there). Run by all threads of a workgroup.
-// COHERENT reads the partials with agent-scope loads (partials written in the
-// same launch).
-template <bool COHERENT, typename BaseOf>
+template <typename BaseOf>
 __device__ __forceinline__ void merge_partials(const float *part_o, const float *part_lse, int n, BaseOf base_of,
                                                int G, int Hq, int b, int g, uint16_t *out, float *lse)
 {
     constexpr int D = kHeadDim;
-    auto ld = [](const float *p) { return COHERENT ? load_coherent(p) : *p; };
     for (int idx = threadIdx.x; idx < G * 32; idx += kDecodeThreads) {
         const int h = idx >> 5, d4 = (idx & 31) * 4;
         float M = -INFINITY, den = 0.f;
@@ -504,12 +501,8 @@ __device__ __forceinline__ void merge_partials(const float *part_o, const float 
 #pragma unroll
             for (int j = 0; j < kMergeBatch; ++j) {
                 const size_t sl = (size_t)base_of(s0 + j < n ? s0 + j : s0) + h;
-                ls[j] = ld(part_lse + sl);
-                const float *po = part_o + sl * D + d4;
-                if (COHERENT)
-                    xs[j] = f32x4{ld(po), ld(po + 1), ld(po + 2), ld(po + 3)};
-                else
-                    xs[j] = *reinterpret_cast<const f32x4 *>(po);
+                ls[j] = part_lse[sl];
+                xs[j] = *reinterpret_cast<const f32x4 *>(part_o + sl * D + d4);
             }
             merge_fold(M, den, o, ls, xs, n - s0);
         }
@@ -530,11 +523,12 @@ struct DecodeLds {
     float m[kWaves][kMaxGroup * NCB];
     float l[kWaves][kMaxGroup * NCB];
     float e[kWaves][kMaxGroup * NCB];
-    int red[2 * kWaves];
+    int red[3 * kWaves];
     // single launch: the split pairs this workgroup arrived at last, merged
     // after its block loop (at most two: only a first and a last segment split)
     int npend;
     int pend[2][5];   // b, g, nseg, wfirst, first_off
+    int pend_last[2];   // this workgroup brought the pair's counter to nseg
     float vs[kMaxGroup * NCB];   // SRC_SHARED: V scale of each query row
 };
 
@@ -559,6 +553,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
     constexpr int D = kHeadDim;
     constexpr int EB = KVFP8 ? 1 : 2;             // bytes per cached element
     constexpr int kSlots = 2;                      // slices in flight per wave
+    constexpr bool kEarlyRefill = NCB == 1;        // refill a slot before its block's math
     const size_t page_head_bytes = (size_t)a.P * D * EB;
 
     // ---- single launch: this workgroup's share of the plan ---------------
@@ -582,16 +577,14 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
             }
             sum += n;
         }
-        int maxle, bits;
-        block_max_or<kDecodeThreads>(mx, bad, lds.red, &maxle, &bits);
+        int maxle, bits, total;
+        int run = block_scan_max_or<kDecodeThreads>(sum, mx, bad, lds.red, &total, &maxle, &bits);
         maxle = __builtin_amdgcn_readfirstlane(maxle);
         bits = __builtin_amdgcn_readfirstlane(bits);
+        total = __builtin_amdgcn_readfirstlane(total);
         if (bits && w == 0 && tid == 0)
             atomicOr(reinterpret_cast<unsigned *>(a.header + H_STATUS), 1u);
         if (SRC == SRC_FUSED_DYNAMIC) {
-            int total;
-            int run = block_excl_scan<kDecodeThreads>(sum, lds.red, &total);
-            total = __builtin_amdgcn_readfirstlane(total);
             for (int bb = b0; bb < b1; ++bb) {
                 run += lds.tp[bb + 1];
                 lds.tp[bb + 1] = run;
@@ -643,11 +636,6 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
 
     Walker<SRC> wk;
     wk.init(&a, w, wave, lds.tp, lds.len, N, We, chunk);
-    const int nblk = wk.count_blocks();
-    if (SRC == SRC_FUSED_DYNAMIC) {
-        wk.ltp = wk.llen = nullptr;   // from here on the walker reads lengths from memory
-        __syncthreads();   // every wave is done with the LDS prefix; lds.acc may now be written
-    }
 
     // per-wave softmax state, head = row. m_run is uniform over the 4 row
     // groups; l_run is this lane's partial sum, reduced at segment end.
@@ -677,8 +665,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
 
     // ---- loads of one block into a slot ---------------------------------
     // K/V loads are issued for every slot, also past the end of the work or
-    // for an empty or invalid slice (then from page 0, which always exists, and
-    // never used), so the number of vector loads between any two points of the
+    // for an empty or invalid slice (then with an empty range: no memory
+    // access), so the number of vector loads between any two points of the
     // pipeline is fixed and the wait before each compute covers its own slot only.
     // q of query rows 16 cb .. 16 cb + 15 of a segment: row r is head r % G of
     // request b + r / G (a shared prefix stacks m requests; rows past m G
@@ -709,47 +697,56 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
         }
     };
 
-    auto issue = [&](Slot &s, Meta &mt) {
-        mt = wk.next();
-        if (mt.valid && mt.first) {
-            // q of (b, g) as the B operand: head = row. Branch-free: rows >= G
-            // read head 0 and are zeroed when copied at the segment's first block,
-            // so nothing here waits for the load and no divergent control flow
-            // separates the scalar bookkeeping of the pipeline.
-            load_q(s.q, mt, 0, mt.ksc, mt.vsc);
-        }
-        // The slab address is wave-uniform (scalar registers); each lane adds its
-        // fixed 32-bit offset (16 bytes per lane, 1 KB per load), so the loads
-        // take the scalar-base form and no 64-bit address arithmetic runs per lane.
-        size_t slab = (size_t)mt.g * page_head_bytes;   // page 0 of kv head g
-        if (mt.valid && mt.nv > 0) {
-            const int tok = mt.tbase + mt.tok0;   // token index in the request
-            const int page = ldc(a.page_table, (size_t)mt.b * a.pt_stride + tok / a.P);
+    // Describe the slot's next block; a segment's first block also brings q
+    // (query rows as the B operand: head = row). Branch-free: rows >= G read
+    // head 0 and are zeroed when copied at the segment's first block, so
+    // nothing here waits for the load and no divergent control flow separates
+    // the scalar bookkeeping of the pipeline.
+    auto next_block = [&](Slot &s, Meta &m) {
+        m = wk.next();
+        if (m.valid && m.first)
+            load_q(s.q, m, 0, m.ksc, m.vsc);
+    };
+    // page id of a block's slice (a scalar load), or -1 when it has no rows
+    auto slice_page = [&](const Meta &m) -> int {
+        if (!m.valid || m.nv <= 0)
+            return -1;
+        return ldc(a.page_table, (size_t)m.b * a.pt_stride + (m.tbase + m.tok0) / a.P);
+    };
+    // The slice's K and V rows are read through buffer descriptors whose base
+    // is the slice's first row (wave-uniform, scalar registers) and whose
+    // range is exactly its valid rows: a row past the request's length, or a
+    // whole slice past the end of the work or on an invalid page (range 0),
+    // reads as zeros without touching memory. Each lane adds its fixed 32-bit
+    // offset (16 bytes per lane, 1 KB per load).
+    auto load_slice = [&](Slot &s, Meta &m, int page) {
+        size_t slab = 0;
+        int nrec = 0;
+        if (m.valid && m.nv > 0) {
             if (page < 0 || page >= a.num_pages) {
                 bad_page = 1;   // reported once at the end of the kernel
-                mt.nv = 0;
+                m.nv = 0;
             } else {
-                slab = ((size_t)page * a.Hkv + mt.g) * page_head_bytes + (size_t)(tok % a.P) * (D * EB);
+                const int tok = m.tbase + m.tok0;   // token index in the request
+                slab = ((size_t)page * a.Hkv + m.g) * page_head_bytes + (size_t)(tok % a.P) * (D * EB);
+                // (wave-uniform; kept in a scalar register so that the
+                // descriptor is, and the loads need no per-lane loop)
+                nrec = __builtin_amdgcn_readfirstlane(m.nv * (D * EB));
             }
         }
-        if (!mt.valid)
-            slab = 0;
-        const uint8_t *kp = a.k + slab;
-        const uint8_t *vp = a.v + slab;
-        if (KVFP8) {
+        const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.k + slab), 0, nrec, kRsrcWord3);
+        const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.v + slab), 0, nrec, kRsrcWord3);
+        constexpr int NL = KVFP8 ? 2 : 4;
 #pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                s.k[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kp + 1024 * p + 16 * lane));
-                s.v[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vp + 1024 * p + 16 * lane));
-            }
-        } else {
+        for (int i = 0; i < NL; ++i)
+            s.k[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, 16 * lane + 1024 * i, 0, kLoadNT));
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                s.k[kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kp + 1024 * kk + 16 * lane));
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                s.v[kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vp + 1024 * kk + 16 * lane));
-        }
+        for (int i = 0; i < NL; ++i)
+            s.v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, 16 * lane + 1024 * i, 0, kLoadNT));
+    };
+    auto issue = [&](Slot &s, Meta &m) {
+        next_block(s, m);
+        load_slice(s, m, slice_page(m));
     };
 
     // ---- end of a segment: merge the 4 waves and write ------------------
@@ -826,69 +823,59 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
                     a.part_lse[prow] = lse2;
             }
         }
-        if (kFused && !mt.direct) {
-            // Arrival: each wave waits for its coherent partial stores to
-            // complete before the barrier, so they are visible device-wide before
-            // the counter moves. The last of the pair's nseg workgroups resets
-            // the counter and notes the pair; it merges the pair's partials with
-            // coherent loads once its own blocks are done (kept out of the block
-            // loop, the merge code no longer crowds the loop's scalar registers).
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            const int bg = mt.b * a.Hkv + mt.g;
-            if (tid == 0) {
-                const int old = __hip_atomic_fetch_add(a.counters + bg, 1, __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT);
-                if (old == mt.nseg - 1) {   // every arrival of this step is in: leave the counter at 0
-                    __hip_atomic_store(a.counters + bg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    const int k = lds.npend;
-                    if (k < 2) {   // a contiguous unit range splits at most its first and last pair
-                        lds.pend[k][0] = mt.b;
-                        lds.pend[k][1] = mt.g;
-                        lds.pend[k][2] = mt.nseg;
-                        lds.pend[k][3] = mt.wfirst;
-                        lds.pend[k][4] = mt.first_off;
-                        lds.npend = k + 1;
-                    }
-                }
+        if (kFused && !mt.direct && tid == 0) {
+            // The pair's arrival is deferred to the end of this workgroup's
+            // blocks (no wait for the stores here, so the loads in flight keep
+            // streaming). A contiguous unit range splits at most its first and
+            // last pair; a third would break the plan's invariant and is
+            // reported instead of merged.
+            const int k = lds.npend;
+            if (k < 2) {
+                lds.pend[k][0] = mt.b;
+                lds.pend[k][1] = mt.g;
+                lds.pend[k][2] = mt.nseg;
+                lds.pend[k][3] = mt.wfirst;
+                lds.pend[k][4] = mt.first_off;
+                lds.npend = k + 1;
+            } else {
+                atomicOr(reinterpret_cast<unsigned *>(a.header + H_STATUS), kStatusInternal);
             }
         }
         __syncthreads();
     };
 
     // ---- math of one block ----------------------------------------------
-    auto compute = [&](Slot &s, const Meta &mt) {
-        {
-            // Load i of lane l brought slice bytes [1024 i + 16 l, +16): row
-            // (1024 i + 16 l) / RB, column byte (1024 i + 16 l) % RB, RB = D * EB.
-            // Write them to this wave's staging rows, then read back the operand
-            // layout (row = lane % 16, bytes 64 i + 16 * (lane / 16)). LDS
-            // operations of one wave complete in order, so no barrier is needed.
-            constexpr int RB = D * EB;
-            constexpr int NL = KVFP8 ? 2 : 4;
-            uint8_t *sk = lds.stg[wave][0];
-            uint8_t *sv = lds.stg[wave][1];
+    // The slot's K/V registers are staged into LDS first; the slot is then
+    // refilled with the loads of its next block, so those are in flight during
+    // this block's math and every wave keeps kSlots slices in flight.
+    auto compute = [&](Slot &s, Meta &mslot) {
+        const Meta mcopy = mslot;   // the slot's description is replaced by the refill
+        const Meta &mt = kEarlyRefill ? mcopy : mslot;
+        constexpr int NL = KVFP8 ? 2 : 4;
+        // operand registers: the slot's own once it is not refilled before the math
+        u32x4 kbuf[4], vbuf[4];
+        u32x4(&kop)[4] = kEarlyRefill ? kbuf : s.k;
+        u32x4(&vop)[4] = kEarlyRefill ? vbuf : s.v;
+        // Load i of lane l brought slice bytes [1024 i + 16 l, +16): row
+        // (1024 i + 16 l) / RB, column byte (1024 i + 16 l) % RB, RB = D * EB.
+        // Write them to this wave's staging rows, then read back the operand
+        // layout (row = lane % 16, bytes 64 i + 16 * (lane / 16)). LDS
+        // operations of one wave complete in order, so no barrier is needed.
+        constexpr int RB = D * EB;
+        uint8_t *sk = lds.stg[wave][0];
+        uint8_t *sv = lds.stg[wave][1];
 #pragma unroll
-            for (int i = 0; i < NL; ++i) {
-                const int byte = 1024 * i + 16 * lane;
-                const int o = (byte / RB) * kStgRow + byte % RB;
-                *reinterpret_cast<u32x4 *>(sk + o) = s.k[i];
-                *reinterpret_cast<u32x4 *>(sv + o) = s.v[i];
-            }
-#pragma unroll
-            for (int i = 0; i < NL; ++i) {
-                const int o = row * kStgRow + 64 * i + 16 * grp;
-                s.k[i] = *reinterpret_cast<const u32x4 *>(sk + o);
-                s.v[i] = *reinterpret_cast<const u32x4 *>(sv + o);
-            }
+        for (int i = 0; i < NL; ++i) {
+            const int byte = 1024 * i + 16 * lane;
+            const int o = (byte / RB) * kStgRow + byte % RB;
+            *reinterpret_cast<u32x4 *>(sk + o) = s.k[i];
+            *reinterpret_cast<u32x4 *>(sv + o) = s.v[i];
         }
-        // K/V registers are consumed on every path (the math runs even for an
-        // empty slice and then contributes nothing); q only at a segment's
-        // first block, which is the only block that loads it.
         // the second column block only when the segment's rows reach it
         // (wave-uniform: a shared item of more than 16 query rows)
         const bool two = NCB == 2 && mt.m * G > 16;
         if (mt.first) {
+            // q arrived with this slot (only a segment's first block loads it)
             float ksc1 = 1.f, vsc1 = 1.f;
             if (NCB == 2 && two)   // loaded here, once per segment (a memory round trip)
                 load_q(qreg[NCB - 1], mt, 1, ksc1, vsc1);
@@ -909,6 +896,17 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
                 vsc_run[cb] = cb == 0 ? mt.vsc : vsc1;
             }
         }
+        // (the two-column-block kernel refills after its math: its second
+        // block's state leaves no registers for a slice in flight beside the
+        // operands)
+        if (kEarlyRefill)
+            issue(s, mslot);
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int o = row * kStgRow + 64 * i + 16 * grp;
+            kop[i] = *reinterpret_cast<const u32x4 *>(sk + o);
+            vop[i] = *reinterpret_cast<const u32x4 *>(sv + o);
+        }
         {
             // scores: S^T[token 4*grp+i][head row], per column block
             f32x4 st[NCB];
@@ -918,8 +916,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
             if (KVFP8) {
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
-                    const uint32_t w0 = s.k[kk >> 1][2 * (kk & 1)];
-                    const uint32_t w1 = s.k[kk >> 1][2 * (kk & 1) + 1];
+                    const uint32_t w0 = kop[kk >> 1][2 * (kk & 1)];
+                    const uint32_t w1 = kop[kk >> 1][2 * (kk & 1) + 1];
                     const bf16x2 c0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
                     const bf16x2 c1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
                     const bf16x2 c2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
@@ -937,7 +935,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
                     if (cb == 0 || two) {
 #pragma unroll
                         for (int kk = 0; kk < 4; ++kk)
-                            st[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, s.k[kk]),
+                            st[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop[kk]),
                                                                              __builtin_bit_cast(bf16x8, qreg[cb][kk]),
                                                                              st[cb], 0, 0, 0);
                     }
@@ -983,12 +981,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
                 l_run[cb] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
                 e_run[cb] += (p[0] + p[1]) + (p[2] + p[3]);
             }
-            // rows past the length may hold anything (NaN): zero them
-            if (mt.nv < kSlice && row >= mt.nv) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    s.v[i] = u32x4{0u, 0u, 0u, 0u};
-            }
+            // rows past the length were read as zeros (the loads' range ends at
+            // the last valid row), so they add nothing to P.V
             const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
@@ -996,11 +990,11 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
                 for (int ss = 0; ss < 2; ++ss) {
                     f32x4 t;
                     if (KVFP8) {
-                        const u32x2 src = {s.v[kk >> 1][2 * (kk & 1)], s.v[kk >> 1][2 * (kk & 1) + 1]};
+                        const u32x2 src = {vop[kk >> 1][2 * (kk & 1)], vop[kk >> 1][2 * (kk & 1) + 1]};
                         t = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(__builtin_bit_cast(long, src),
                                                                        (long)sel8[ss], zero, 0, 0, 0);
                     } else {
-                        t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, s.v[kk]),
+                        t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vop[kk]),
                                                                     sel16[ss], zero, 0, 0, 0);
                     }
                     const s16x4 vt = pack_bf16x4(t);
@@ -1014,6 +1008,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
         }
         if (mt.last)
             finish(mt);
+        if (!kEarlyRefill)
+            issue(s, mslot);
     };
 
     // ---- software pipeline: kSlots slices in flight per wave --------------
@@ -1023,23 +1019,85 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
     // no more useful bytes in flight.)
     Slot sl[kSlots];
     Meta mt[kSlots];
+    {
+        // the first blocks' page ids are fetched together (one round trip)
+        int pg[kSlots];
+#pragma unroll
+        for (int i = 0; i < kSlots; ++i)
+            next_block(sl[i], mt[i]);
+#pragma unroll
+        for (int i = 0; i < kSlots; ++i)
+            pg[i] = slice_page(mt[i]);
+#pragma unroll
+        for (int i = 0; i < kSlots; ++i)
+            load_slice(sl[i], mt[i], pg[i]);
+    }
+    // the block count is walked while the first slices are in flight: the
+    // blocks still ahead of the walker plus those already issued
+    int nblk = wk.count_blocks();
 #pragma unroll
     for (int i = 0; i < kSlots; ++i)
-        issue(sl[i], mt[i]);
+        nblk += mt[i].valid;
+    if (SRC == SRC_FUSED_DYNAMIC) {
+        wk.ltp = wk.llen = nullptr;   // from here on the walker reads lengths from memory
+        __syncthreads();   // every wave is done with the LDS prefix, which the staging rows alias
+    }
     for (int it = 0; it < nblk; it += kSlots) {
         set_progress_priority(it, nblk);
 #pragma unroll
-        for (int i = 0; i < kSlots; ++i) {
+        for (int i = 0; i < kSlots; ++i)
             compute(sl[i], mt[i]);
-            issue(sl[i], mt[i]);
-        }
     }
 
-    // single launch: merge the pairs this workgroup arrived at last
+    // single launch: arrive at the split pairs and merge those this workgroup
+    // completes. Ordering across workgroups:
+    //  * every partial was stored with agent-scope (device-coherent) stores,
+    //    which write through this XCD's L2; each wave waits for its stores to
+    //    complete (s_waitcnt 0, the stores' acknowledgement from the device's
+    //    coherence point) before the barrier, and only then does thread 0 add
+    //    this workgroup's arrival (an agent-scope atomic, performed at that
+    //    same coherence point);
+    //  * the workgroup whose addition brings a pair's counter to its number of
+    //    pieces has seen every other piece's arrival, hence the completion of
+    //    their stores; it then runs an agent-scope acquire fence (invalidating
+    //    this XCD's caches) before its merge reads the partials, so those reads
+    //    cannot return data cached before the stores.
+    // A release ordering on the arrival would write back this XCD's whole L2
+    // at every workgroup's end (measured 7-12% slower); the device-coherent
+    // stores plus the completion wait give the same order for the partials,
+    // the only data the counter publishes. The merging workgroup leaves the
+    // counter at 0 for the next step.
     if (kFused) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const int np = lds.npend;
+            int old[2] = {0, 0};
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+                if (k < np)
+                    old[k] = __hip_atomic_fetch_add(a.counters + lds.pend[k][0] * a.Hkv + lds.pend[k][1], 1,
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            int any = 0;
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                if (k < np) {
+                    const int last = old[k] == lds.pend[k][2] - 1;
+                    if (last)
+                        __hip_atomic_store(a.counters + lds.pend[k][0] * a.Hkv + lds.pend[k][1], 0,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    lds.pend_last[k] = last;
+                    any |= last;
+                }
+            }
+            if (any)
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
         __syncthreads();
         const int np = __builtin_amdgcn_readfirstlane(lds.npend);
         for (int k = 0; k < np; ++k) {
+            if (!__builtin_amdgcn_readfirstlane(lds.pend_last[k]))
+                continue;
             const int pb = __builtin_amdgcn_readfirstlane(lds.pend[k][0]);
             const int pg = __builtin_amdgcn_readfirstlane(lds.pend[k][1]);
             const int pn = __builtin_amdgcn_readfirstlane(lds.pend[k][2]);
@@ -1047,13 +1105,13 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
             const int off = __builtin_amdgcn_readfirstlane(lds.pend[k][4]);
             const int sr = a.slot_rows;
             if (SRC == SRC_FUSED_DYNAMIC) {
-                merge_partials<true>(a.part_o, a.part_lse, pn,
-                                     [=](int s) { return (2 * (wf + s) + (s == 0 ? off : 0)) * sr; }, G, a.Hq,
-                                     pb, pg, a.out, a.lse);
+                merge_partials(a.part_o, a.part_lse, pn,
+                               [=](int s) { return (2 * (wf + s) + (s == 0 ? off : 0)) * sr; }, G, a.Hq, pb, pg,
+                               a.out, a.lse);
             } else {
                 const int s0 = (pb * a.Hkv + pg) * a.S;
-                merge_partials<true>(a.part_o, a.part_lse, pn, [=](int s) { return (s0 + s) * sr; }, G, a.Hq, pb,
-                                     pg, a.out, a.lse);
+                merge_partials(a.part_o, a.part_lse, pn, [=](int s) { return (s0 + s) * sr; }, G, a.Hq, pb, pg,
+                               a.out, a.lse);
             }
         }
     }
@@ -1079,7 +1137,7 @@ __global__ __launch_bounds__(kDecodeThreads) void combine_kernel(CombineArgs a)
     if (n == 1)
         return;
     const int sr = a.slot_rows;
-    merge_partials<false>(a.part_o, a.part_lse, n, [=](int s) { return (s0 + s) * sr; }, a.G, a.Hq, b, g, a.out,
+    merge_partials(a.part_o, a.part_lse, n, [=](int s) { return (s0 + s) * sr; }, a.G, a.Hq, b, g, a.out,
                           a.lse);
 }
 
@@ -1100,7 +1158,7 @@ __global__ __launch_bounds__(kDecodeThreads) void combine_shared_kernel(CombineA
         ns = a.seg_prefix[is * a.Hkv + g + 1] - s0;
     }
     const int sr = a.slot_rows, off = a.req_member[b] * a.G;
-    merge_partials<false>(a.part_o, a.part_lse, ns + no,
+    merge_partials(a.part_o, a.part_lse, ns + no,
                           [=](int s) { return s < ns ? (s0 + s) * sr + off : (o0 + s - ns) * sr; }, a.G, a.Hq, b,
                           g, a.out, a.lse);
 }

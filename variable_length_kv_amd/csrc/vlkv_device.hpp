@@ -60,6 +60,42 @@ __device__ __forceinline__ int block_excl_scan(int v, int *lds, int *total)
     return before + incl - v;
 }
 
+// Exclusive prefix sum of one int per thread over a workgroup of NT threads
+// (in thread order), with the workgroup's maximum of a second int and OR of a
+// third, through a single barrier. *total receives the sum over all threads.
+// `lds` holds 3*NT/64 ints and must not be written again before the caller's
+// next barrier. Every thread of the workgroup must call it.
+template <int NT>
+__device__ __forceinline__ int block_scan_max_or(int v, int mx, int bits, int *lds, int *total, int *mx_out,
+                                                 int *bits_out)
+{
+    constexpr int NW = NT / 64;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int incl = wave_incl_scan(v);
+    mx = wave_max(mx);
+    bits = wave_or(bits);
+    if (lane == 63)
+        lds[wave] = incl;
+    if (lane == 0) {
+        lds[NW + wave] = mx;
+        lds[2 * NW + wave] = bits;
+    }
+    __syncthreads();
+    int before = 0, all = 0, m = 0, o = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const int t = lds[i];
+        before += i < wave ? t : 0;
+        all += t;
+        m = max(m, lds[NW + i]);
+        o |= lds[2 * NW + i];
+    }
+    *total = all;
+    *mx_out = m;
+    *bits_out = o;
+    return before + incl - v;
+}
+
 // Exclusive running maximum of one int per thread over a workgroup of NT
 // threads (in thread order); `lo` is the identity (returned to thread 0).
 // `lds` holds NT/64 ints. Every thread of the workgroup must call it.

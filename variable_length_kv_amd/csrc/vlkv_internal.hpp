@@ -16,6 +16,8 @@ constexpr int kDecodeThreads = 256;
 constexpr int kMaxGroup = 16;      // query heads per kv head (one MFMA column block)
 constexpr int kMaxBatch = 8192;    // planner keeps the tile prefix in LDS
 constexpr int kHeaderInts = 8;
+// status word bit for a broken plan invariant (ATTN_STATUS_INTERNAL)
+constexpr unsigned kStatusInternal = 4u;
 
 // header fields (mode 2: H_CHUNK holds the number of items, H_SPLITS the
 // requests per shared pass R)

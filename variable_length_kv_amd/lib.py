@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libvlkv_attn.so")
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
 ATTN_KV_BF16, ATTN_KV_FP8_E4M3 = 0, 1
 ATTN_DYNAMIC, ATTN_STATIC, ATTN_SHARED = 0, 1, 2
-ATTN_STATUS_BAD_LENGTH, ATTN_STATUS_BAD_PAGE = 1, 2
+ATTN_STATUS_BAD_LENGTH, ATTN_STATUS_BAD_PAGE, ATTN_STATUS_INTERNAL = 1, 2, 4
 
 EXPORTED = ("attn_check_shape", "attn_workspace_bytes", "attn_static_splits", "attn_device_cu_count",
             "attn_plan", "attn_decode", "attn_combine", "attn_get_status", "attn_read_plan",
