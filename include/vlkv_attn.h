@@ -30,7 +30,8 @@
  *     never waited for, except by attn_get_status.
  *   - The caller allocates and owns every buffer. The library allocates no
  *     memory, keeps no pointer after a call returns and has no global mutable
- *     state; calls on different workspaces may run concurrently.
+ *     state (apart from the per-GPU scratch of attn_step_noalloc); calls on
+ *     different workspaces may run concurrently.
  *   - Return value: ATTN_OK, or an ATTN_ERR_* code. Argument and shape checks
  *     happen on the host before anything is enqueued; on error nothing is
  *     enqueued and attn_last_error() describes the problem.
@@ -218,6 +219,34 @@ int attn_step(const attn_shape *shape, const void *q, const void *k_cache, const
               const float *k_scale, const float *v_scale, const int32_t *page_table,
               const int32_t *lengths, float sm_scale, void *workspace, size_t workspace_bytes,
               void *out, float *lse, void *stream);
+
+/*
+ * attn_step for callers that cannot allocate device memory: code under HIP
+ * graph capture, serving loops and harnesses that forbid hipMalloc. Arguments
+ * and results as in attn_step, without the workspace: the step's arrival
+ * counters, partial results and a status word live in a fixed scratch array
+ * inside this library's device code, one per GPU, of
+ * ATTN_NOALLOC_SCRATCH_BYTES bytes (placed when the library is first used on a
+ * GPU and held until the process ends). This call allocates nothing.
+ *   status  (device, optional) uint32: the step ORs its ATTN_STATUS_* bits into
+ *           it (the caller clears it); NULL keeps them in the scratch, unread.
+ * Limits, checked on the host (ATTN_ERR_INVALID_ARG, nothing enqueued):
+ * batch * num_kv_heads <= ATTN_NOALLOC_MAX_PAIRS, and the partial results must
+ * fit the scratch: 2 * num_wgs slots (ATTN_DYNAMIC) or batch * num_kv_heads * S
+ * slots (ATTN_STATIC), each Hq/Hkv rows of head_dim + 1 floats, plus 256 bytes
+ * of alignment, at most ATTN_NOALLOC_SCRATCH_BYTES - 4 * ATTN_NOALLOC_MAX_PAIRS
+ * - 256 bytes. ATTN_SHARED returns ATTN_ERR_UNSUPPORTED (its plan needs a
+ * workspace). Every call on a GPU shares that GPU's scratch: calls that can
+ * overlap on one GPU (different streams without ordering between them) race
+ * and give wrong results. The first call on a GPU also enqueues one small
+ * kernel that clears the arrival counters; every step leaves them at zero.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES (16u << 20)
+#define ATTN_NOALLOC_MAX_PAIRS     65536
+int attn_step_noalloc(const attn_shape *shape, const void *q, const void *k_cache,
+                      const void *v_cache, const float *k_scale, const float *v_scale,
+                      const int32_t *page_table, const int32_t *lengths, float sm_scale,
+                      void *out, float *lse, uint32_t *status, void *stream);
 
 /*
  * Append one new token per request to the paged caches: the step that grows

@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/vlkv_attn.h"
@@ -410,50 +411,46 @@ int attn_workspace_init(const attn_shape *shape, void *workspace, size_t workspa
     return ok();
 }
 
-int attn_step(const attn_shape *shape, const void *q, const void *k_cache, const void *v_cache,
-              const float *k_scale, const float *v_scale, const int32_t *page_table,
-              const int32_t *lengths, float sm_scale, void *workspace, size_t workspace_bytes,
-              void *out, float *lse, void *stream)
+// Checks shared by attn_step and attn_step_noalloc (everything but the
+// workspace).
+static int check_step_args(const attn_shape *shape, Shape *s, const void *q, const void *k_cache,
+                           const void *v_cache, const float *k_scale, const float *v_scale,
+                           const int32_t *page_table, const int32_t *lengths, float sm_scale, const void *out)
 {
-    Shape s;
-    WsLayout L;
-    int rc = check(shape, &s);
+    int rc = check(shape, s);
     if (rc != ATTN_OK)
         return rc;
     if (!q || !k_cache || !v_cache || !page_table || !lengths || !out)
         return fail(ATTN_ERR_INVALID_ARG, "q, k_cache, v_cache, page_table, lengths and out must be non-NULL");
-    if (s.kv_fp8 && (!k_scale || !v_scale))
+    if (s->kv_fp8 && (!k_scale || !v_scale))
         return fail(ATTN_ERR_INVALID_ARG, "fp8 cache needs k_scale and v_scale");
     if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY)
         return fail(ATTN_ERR_INVALID_ARG, "sm_scale is not finite");
     if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
          reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(out)) % 16)
         return fail(ATTN_ERR_INVALID_ARG, "q, caches and out must be 16-byte aligned");
-    if ((rc = check_ws(s, workspace, workspace_bytes, &L)) != ATTN_OK)
-        return rc;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    if (s.mode == ATTN_SHARED) {
-        // the prefix-shared plan groups requests by comparing page tables; it
-        // runs as its own launch, followed by the decode and the combine
-        if ((rc = enqueue_plan(s, L, lengths, page_table, workspace, st)) != ATTN_OK)
-            return rc;
-        if ((rc = enqueue_decode(s, L, q, k_cache, v_cache, k_scale, v_scale, page_table, sm_scale, workspace, out,
-                                 lse, st)) != ATTN_OK)
-            return rc;
-        return enqueue_combine(s, L, workspace, out, lse, st);
-    }
+    return ATTN_OK;
+}
+
+// The single-launch step (dynamic or static) on the given arrival counters,
+// status word and partial-result arrays.
+static int enqueue_step(const Shape &s, const void *q, const void *k_cache, const void *v_cache,
+                        const float *k_scale, const float *v_scale, const int32_t *page_table,
+                        const int32_t *lengths, float sm_scale, int32_t *counters, int32_t *status,
+                        float *part_o, float *part_lse, int slot_rows, void *out, float *lse, hipStream_t st)
+{
     DecodeArgs a{};
     a.lengths = lengths;
-    a.counters = at<int32_t>(workspace, L.counters);
+    a.counters = counters;
     a.q = static_cast<const uint16_t *>(q);
     a.k = static_cast<const uint8_t *>(k_cache);
     a.v = static_cast<const uint8_t *>(v_cache);
     a.k_scale = k_scale;
     a.v_scale = v_scale;
     a.page_table = page_table;
-    a.header = at<int32_t>(workspace, L.header);
-    a.part_o = at<float>(workspace, L.part_o);
-    a.part_lse = at<float>(workspace, L.part_lse);
+    a.header = status;   // the single launch uses only the status word (H_STATUS = 0)
+    a.part_o = part_o;
+    a.part_lse = part_lse;
     a.out = static_cast<uint16_t *>(out);
     a.lse = lse;
     a.B = s.B;
@@ -467,7 +464,7 @@ int attn_step(const attn_shape *shape, const void *q, const void *k_cache, const
     a.S = s.S;
     a.T = s.T;
     a.W = s.W;
-    a.slot_rows = L.slot_rows;
+    a.slot_rows = slot_rows;
     a.scale_log2 = sm_scale * 1.4426950408889634f;
     const int grid = s.mode == ATTN_STATIC ? s.B * s.Hkv * s.S : s.W;
     const hipError_t e = launch_decode(a, s.mode == ATTN_STATIC ? SRC_FUSED_STATIC : SRC_FUSED_DYNAMIC,
@@ -475,6 +472,128 @@ int attn_step(const attn_shape *shape, const void *q, const void *k_cache, const
     if (e != hipSuccess)
         return hip_fail(e, "step launch");
     return ok();
+}
+
+int attn_step(const attn_shape *shape, const void *q, const void *k_cache, const void *v_cache,
+              const float *k_scale, const float *v_scale, const int32_t *page_table,
+              const int32_t *lengths, float sm_scale, void *workspace, size_t workspace_bytes,
+              void *out, float *lse, void *stream)
+{
+    Shape s;
+    WsLayout L;
+    int rc = check_step_args(shape, &s, q, k_cache, v_cache, k_scale, v_scale, page_table, lengths, sm_scale, out);
+    if (rc != ATTN_OK)
+        return rc;
+    if ((rc = check_ws(s, workspace, workspace_bytes, &L)) != ATTN_OK)
+        return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (s.mode == ATTN_SHARED) {
+        // the prefix-shared plan groups requests by comparing page tables; it
+        // runs as its own launch, followed by the decode and the combine
+        if ((rc = enqueue_plan(s, L, lengths, page_table, workspace, st)) != ATTN_OK)
+            return rc;
+        if ((rc = enqueue_decode(s, L, q, k_cache, v_cache, k_scale, v_scale, page_table, sm_scale, workspace, out,
+                                 lse, st)) != ATTN_OK)
+            return rc;
+        return enqueue_combine(s, L, workspace, out, lse, st);
+    }
+    return enqueue_step(s, q, k_cache, v_cache, k_scale, v_scale, page_table, lengths, sm_scale,
+                        at<int32_t>(workspace, L.counters), at<int32_t>(workspace, L.header),
+                        at<float>(workspace, L.part_o), at<float>(workspace, L.part_lse), L.slot_rows, out, lse, st);
+}
+
+}  // extern "C"
+
+// ---- attn_step_noalloc: the step without a caller workspace -----------------
+// Its scratch (arrival counters, a status word, partial results) is this
+// file-scope device array: one copy per GPU, placed when the library's code
+// object is loaded on that GPU and held until the process ends. Host code never
+// passes `scratch` itself to a kernel (on the host the name is only a stand-in);
+// it uses the device address that hipGetSymbolAddress returns for the current
+// GPU, taken once per GPU at its first call.
+namespace vlkv {
+namespace {
+
+constexpr size_t kScratchBytes = ATTN_NOALLOC_SCRATCH_BYTES;
+constexpr int64_t kScratchPairs = ATTN_NOALLOC_MAX_PAIRS;
+constexpr size_t kScratchCounters = 0;                                     // int32 [kScratchPairs]
+constexpr size_t kScratchStatus = kScratchPairs * sizeof(int32_t);         // int32 [kHeaderInts]
+constexpr size_t kScratchParts = kScratchStatus + 256;                     // part_lse, then part_o
+static_assert(kScratchStatus % 256 == 0, "scratch regions must stay 256-byte aligned");
+
+__device__ __align__(256) static uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+uint8_t *g_scratch_ptr[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Partial-result bytes the single launch needs for this shape: two slots per
+// workgroup (its first and last segment) in dynamic mode, S per (request, kv
+// head) in static mode; each slot holds G rows of (D + 1) floats.
+size_t noalloc_parts_bytes(const Shape &s, int64_t *slots)
+{
+    *slots = s.mode == ATTN_STATIC ? (int64_t)s.B * s.Hkv * s.S : 2 * (int64_t)s.W;
+    return align256((size_t)*slots * s.G * sizeof(float)) + (size_t)*slots * s.G * s.D * sizeof(float);
+}
+
+}  // namespace
+}  // namespace vlkv
+
+extern "C" {
+
+int attn_step_noalloc(const attn_shape *shape, const void *q, const void *k_cache, const void *v_cache,
+                      const float *k_scale, const float *v_scale, const int32_t *page_table,
+                      const int32_t *lengths, float sm_scale, void *out, float *lse, uint32_t *status,
+                      void *stream)
+{
+    Shape s;
+    int rc = check_step_args(shape, &s, q, k_cache, v_cache, k_scale, v_scale, page_table, lengths, sm_scale, out);
+    if (rc != ATTN_OK)
+        return rc;
+    if (s.mode == ATTN_SHARED)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_step_noalloc: mode ATTN_SHARED needs a workspace (attn_step)");
+    if ((int64_t)s.B * s.Hkv > kScratchPairs)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_step_noalloc: batch * num_kv_heads = %lld exceeds the scratch limit %lld",
+                    (long long)s.B * s.Hkv, (long long)kScratchPairs);
+    int64_t slots;
+    const size_t parts = noalloc_parts_bytes(s, &slots);
+    if (parts > kScratchBytes - kScratchParts)
+        return fail(ATTN_ERR_INVALID_ARG,
+                    "attn_step_noalloc: %lld partial slots need %zu bytes, more than the %zu-byte scratch holds",
+                    (long long)slots, parts, kScratchBytes - kScratchParts);
+    if (reinterpret_cast<uintptr_t>(status) % 4)
+        return fail(ATTN_ERR_INVALID_ARG, "status must be 4-byte aligned");
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_step_noalloc: device %d beyond the %d it serves", dev, kMaxDevices);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    bool first = false;
+    std::call_once(g_scratch_once[dev], [&] {
+        void *p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = static_cast<uint8_t *>(p);
+        first = true;
+    });
+    if (g_scratch_err[dev] != hipSuccess)
+        return hip_fail(g_scratch_err[dev], "hipGetSymbolAddress(scratch)");
+    uint8_t *base = g_scratch_ptr[dev];
+    int32_t *counters = reinterpret_cast<int32_t *>(base + kScratchCounters);
+    int32_t *own_status = reinterpret_cast<int32_t *>(base + kScratchStatus);
+    if (first) {
+        // the counters must start at zero (every completed step leaves them
+        // there); cleared by a fill kernel on the caller's stream, not a memset
+        if ((e = launch_ws_init(own_status, counters, (int)kScratchPairs, st)) != hipSuccess)
+            return hip_fail(e, "scratch init launch");
+    }
+    float *part_lse = reinterpret_cast<float *>(base + kScratchParts);
+    float *part_o = reinterpret_cast<float *>(base + kScratchParts + align256((size_t)slots * s.G * sizeof(float)));
+    return enqueue_step(s, q, k_cache, v_cache, k_scale, v_scale, page_table, lengths, sm_scale, counters,
+                        status ? reinterpret_cast<int32_t *>(status) : own_status, part_o, part_lse, s.G, out, lse,
+                        st);
 }
 
 int attn_append_kv(const attn_shape *shape, const void *k_new, const void *v_new, const int32_t *positions,

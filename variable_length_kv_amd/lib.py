@@ -24,7 +24,8 @@ ATTN_STATUS_BAD_LENGTH, ATTN_STATUS_BAD_PAGE, ATTN_STATUS_INTERNAL = 1, 2, 4
 
 EXPORTED = ("attn_check_shape", "attn_workspace_bytes", "attn_static_splits", "attn_device_cu_count",
             "attn_plan", "attn_decode", "attn_combine", "attn_get_status", "attn_read_plan",
-            "attn_workspace_init", "attn_step", "attn_append_kv", "attn_read_plan_items", "attn_last_error",
+            "attn_workspace_init", "attn_step", "attn_step_noalloc", "attn_append_kv", "attn_read_plan_items",
+            "attn_last_error",
             "router_split_weights", "router_workspace_bytes", "router_gemm")
 
 
@@ -86,6 +87,7 @@ def load():
         "attn_read_plan": (i32, [SP, P, P, P, P, P, P, P, P, P]),
         "attn_workspace_init": (i32, [SP, P, sz, P]),
         "attn_step": (i32, [SP, P, P, P, P, P, P, P, ctypes.c_float, P, sz, P, P, P]),
+        "attn_step_noalloc": (i32, [SP, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P]),
         "attn_append_kv": (i32, [SP, P, P, P, P, P, P, P, P, P, sz, P]),
         "attn_read_plan_items": (i32, [SP, P, P, P, P, P, P, P, P, P]),
         "router_split_weights": (i32, [P, P, P, ctypes.c_int64, P]),
@@ -264,6 +266,19 @@ def attn_step(shape, q, k_cache, v_cache, k_scale, v_scale, page_table, lengths,
     _check(load().attn_step(_shape(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
                             _ptr(page_table), _ptr(lengths), float(sm_scale), _ptr(workspace),
                             workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def attn_step_noalloc(shape, q, k_cache, v_cache, k_scale, v_scale, page_table, lengths, sm_scale, out,
+                      lse=None, status=None, stream=None) -> None:
+    """attn_step without a workspace (the library's per-GPU scratch; see the C
+    header). ``status``: optional int32 device tensor of one element that
+    receives the step's status bits."""
+    _need_step(shape, q, k_cache, v_cache, k_scale, v_scale, page_table, lengths, out, lse)
+    _need(status, "status", _I32, 1, optional=True)
+    _on_gpu(status=status)
+    _check(load().attn_step_noalloc(_shape(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                    _ptr(v_scale), _ptr(page_table), _ptr(lengths), float(sm_scale), _ptr(out),
+                                    _ptr(lse), _ptr(status), _stream(stream)))
 
 
 def attn_append_kv(shape, k_new, v_new, positions, page_table, k_cache, v_cache, k_scale=None, v_scale=None,
