@@ -4,26 +4,30 @@ C ABI of libvlkv_attn.so.
 Headline workload: 32 requests with context lengths uniform in [1000, 16000],
 64 query / 8 kv heads, head dim 128, bf16 paged cache with 64-token pages and a
 random page table. A step is one decode step over the whole batch: the tile
-plan for the current lengths, the split-KV decode and the log-sum-exp merge.
-The headline step is attn_step (all three in one kernel launch); the
-three-launch form (attn_plan + attn_decode + attn_combine) is timed too. After
---settle-s seconds of untimed steps (GPU clocks out of idle) and W warm-up
-steps, K steps run back to back between two device synchronisations. The figure of
-merit is effective KV bandwidth: every cached K and V row of the batch once
-(2 * Hkv * D * 2 bytes per token) divided by the step time.
+plan for the current lengths, the split-KV decode and the log-sum-exp merge,
+all in one launch (attn_step); the three-launch form (attn_plan + attn_decode +
+attn_combine) is timed too. After --settle-s seconds of untimed steps (GPU
+clocks out of idle) and W warm-up steps, K steps are timed one at a time with
+HIP events, each after a 1 GiB read sweep that evicts the 256 MB Infinity Cache
+(the sweep is outside the timed region); the median is the step time. The
+figure of merit is effective KV bandwidth: every cached K and V row of the
+batch once (2 * Hkv * D * 2 bytes per token) divided by the step time. The
+same steps back to back are reported beside it.
 
 Also reported (field "extra"): the tiny batch (4 requests, launch-bound), the
-skewed batch (1 x 16000 + 63 x 1000 tokens)
-under the dynamic plan and under the in-library static split-K at its default
-split count and a split sweep, the long-tail batch, and the 256-step
-continuous-batching trace over an fp8 e4m3 cache (plan rebuilt every step;
-the single-launch step also captured once in a HIP graph and replayed).
-Those are timed per step with HIP events, with a 1 GiB read sweep between steps
-so that no step starts with the previous step's data in the 256 MB Infinity
-Cache. The CPU reference is timed on the host as a reported baseline
-("cpu_baseline").
+skewed batch (1 x 16000 + 63 x 1000 tokens) under the dynamic plan and under
+the in-library static split-K at its default split count and a split sweep,
+the long-tail batch, the 256-step continuous-batching trace over an fp8 e4m3
+cache (plan rebuilt every step; the single-launch step also captured once in a
+HIP graph and replayed), prefix caching, and the router GEMM, each timed per
+step after a cache sweep. Every leg keeps a host copy of the outputs it timed;
+the CPU reference leg ("cpu_baseline": the oracle timed on the host as a
+reported baseline) also checks each of them against the oracle ("parity"),
+and the process exits with status 1 if any is out of bounds.
 
 Prints ONE JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Profile summaries: --kernel-stats DIR OUT_JSON, --traffic-summary FETCH_DIR
+WRITE_DIR PROBE_OUTPUT OUT_JSON (rocprofv3 output directories, see profiles/).
 """
 import argparse
 import hashlib
@@ -41,8 +45,13 @@ sys.path.insert(0, ROOT)
 METRIC = "decode-attention µs/step and effective KV GB/s (% of HBM peak), mixed lengths"
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic_uniform_mixed.json")
+KERNEL_STATS_FILE = os.path.join(ROOT, "profiles", "decode_kernel_trace_uniform_mixed.json")
 FUSED_KERNEL = "decode_kernel<2, 0>"     # single launch, dynamic plan, bf16 cache
 THREE_KERNEL = "decode_kernel<0, 0>"     # decode launch of the three-launch step
+# parity bounds against the CPU reference: |o - ref| <= atol + rtol |ref|,
+# per-(request, head) relative L2, and lse within LSE_ATOL
+TOL = {"bf16": (1e-2, 1e-2, 2e-2), "fp8": (5e-2, 5e-2, 6e-2)}
+LSE_ATOL = 1e-3
 
 
 def log(*a):
@@ -62,9 +71,10 @@ def us(x_ms):
 
 
 class Runner:
-    """Device copies of one decode step and Attention objects for it."""
+    """Device copies of one decode step and Attention objects for it (W = 0:
+    the library's default workgroup count)."""
 
-    def __init__(self, case, torch, L, W):
+    def __init__(self, case, torch, L, W=0):
         self.c, self.torch, self.L = case, torch, L
         d = torch.device("cuda:0")
         self.q = case.q.to(d)
@@ -106,6 +116,54 @@ class Runner:
 
     def step(self, att, fused):
         (self.fused if fused else self.three)(att)
+
+    def w_eff(self, att):
+        """Workgroups the dynamic plan of this step uses (from attn_plan's header)."""
+        self.plan(att)
+        self.torch.cuda.synchronize()
+        return int(att.read_plan()["header"][2])
+
+
+# Host copies of the outputs the legs timed, checked against the CPU reference
+# by the cpu_baseline leg (the only part of this file that runs the oracle).
+CAPTURES = []
+
+
+def capture(name, case, out, lse):
+    """Keep (a host copy of) the bf16 outputs and lse of `case` for the parity
+    check."""
+    CAPTURES.append({"name": name, "case": case, "out": out.detach().cpu().clone(),
+                     "lse": lse.detach().cpu().clone()})
+
+
+def capture_sample(name, case, out, lse, ids):
+    """As capture, for the requests `ids` only (a compact copy of their pages)."""
+    from variable_length_kv_amd import workloads as wl
+    ids = sorted(int(i) for i in ids)
+    CAPTURES.append({"name": name, "case": wl.sub_case(case, ids), "out": out.detach().cpu()[ids].clone(),
+                     "lse": lse.detach().cpu()[ids].clone()})
+
+
+def compare(out, lse, ref_o, ref_l, kv_dtype):
+    """Errors of GPU outputs against the CPU reference, and whether they are
+    within the parity bounds."""
+    atol, rtol, l2tol = TOL[kv_dtype]
+    o = out.double().numpy()
+    ls = lse.double().numpy()
+    err = np.abs(o - ref_o)
+    bound = atol + rtol * np.abs(ref_o)
+    finite = bool(np.isfinite(o).all())
+    worst = float((err / bound).max()) if err.size else 0.0
+    fin = np.isfinite(ref_l)
+    lse_shape_ok = bool(np.array_equal(np.isfinite(ls), fin) and np.all(ls[~fin] == -np.inf))
+    lerr = float(np.abs(ls[fin] - ref_l[fin]).max()) if fin.any() else 0.0
+    num = np.linalg.norm((o - ref_o).reshape(-1, o.shape[-1]), axis=1)
+    den = np.linalg.norm(ref_o.reshape(-1, o.shape[-1]), axis=1)
+    rel = float((num[den > 0] / den[den > 0]).max()) if (den > 0).any() else 0.0
+    ok = finite and worst <= 1.0 and lse_shape_ok and lerr <= LSE_ATOL and rel <= l2tol
+    return {"ok": bool(ok), "max_abs_err": float(err.max()) if err.size else 0.0, "worst_err_over_bound": round(worst, 4),
+            "max_lse_err": lerr, "max_rel_l2": round(rel, 5), "requests": int(o.shape[0]),
+            "bound": f"|o-ref| <= {atol:g} + {rtol:g}|ref|, rel L2 <= {l2tol:g}, |lse-ref| <= {LSE_ATOL:g}"}
 
 
 def ev(torch):
@@ -213,16 +271,19 @@ def per_step_flushed(run, att, steps, warmup, torch, flush, fused):
     return np.array(ts)
 
 
-def cpu_baseline(case, budget_s=10.0):
+def cpu_baseline(case, budget_s=10.0, captures=()):
     """The CPU reference (fp64 C, OpenMP over (request, kv head)) on the same
     workload: whole passes over all requests, repeated until budget_s seconds
-    have been spent (at least one pass)."""
+    have been spent (at least one pass). Then, untimed, the reference for each
+    captured GPU output and its errors against the parity bounds. Returns
+    (baseline, parity)."""
     import oracle
     threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
     passes, t_total = 0, 0.0
+    ref = None
     while passes == 0 or t_total < budget_s:
         t0 = time.perf_counter()
-        oracle.decode(case, threads=threads)
+        ref = oracle.decode(case, threads=threads)
         t_total += time.perf_counter() - t0
         passes += 1
     nbytes = case.kv_bytes * passes
@@ -238,7 +299,7 @@ def cpu_baseline(case, budget_s=10.0):
             model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
     except OSError:
         pass
-    return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+    base = {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{passes} whole passes over the headline workload ({case.B} requests, "
                       f"{case.total_tokens} tokens, {case.kv_bytes / 1e6:.1f} MB of KV each) in "
                       f"{t_total:.1f} s; fp64 C, OpenMP over (request, kv head)",
@@ -246,6 +307,12 @@ def cpu_baseline(case, budget_s=10.0):
             "sample_1_thread": f"requests 0..{len(ids) - 1} of the same workload ({sub_bytes / 1e6:.1f} MB of KV) "
                                f"in {t1:.1f} s on one thread",
             "cpu_model": model}
+    parity = {}
+    for cap in captures:
+        c = cap["case"]
+        ro, rl = ref if c is case else oracle.decode(c, threads=threads)
+        parity[cap["name"]] = compare(cap["out"], cap["lse"], ro, rl, c.kv_dtype)
+    return base, parity
 
 
 def stats(ts_ms, kv_bytes):
@@ -254,21 +321,23 @@ def stats(ts_ms, kv_bytes):
             "pct_hbm": round(100 * kv_bytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
 
 
-def pick_wgs(args, L, cus, lengths, Hkv):
-    """Workgroups of the dynamic plan: --wgs-per-cu if given, else the
-    library's occupancy suggestion for these lengths."""
-    if args.wgs_per_cu > 0:
-        return args.wgs_per_cu * cus
-    return L.suggest_num_wgs(cus, lengths, Hkv)
+def pick_wgs(args, cus):
+    """Workgroups of the launch: --wgs-per-cu if given, else 0 (the library's
+    default: two per compute unit, of which the plan uses one per compute unit
+    on steps too small to give each workgroup 32 tiles)."""
+    return args.wgs_per_cu * cus if args.wgs_per_cu > 0 else 0
 
 
 def batch_leg(cid, torch, L, wl, W_of, flush, static_sweep=False):
     c = wl.config_case(cid)
     W = W_of(c.lengths, c.Hkv)
     r = Runner(c, torch, L, W)
-    entry = {"kv_gb": round(c.kv_bytes / 1e9, 4), "tokens": c.total_tokens, "num_wgs": W}
+    name = {2: "skewed", 3: "long_tail"}[cid]
+    entry = {"kv_gb": round(c.kv_bytes / 1e9, 4), "tokens": c.total_tokens}
     a = r.attention(L.ATTN_DYNAMIC)
+    entry["num_wgs"] = r.w_eff(a)
     entry["dynamic"] = stats(per_step_flushed(r, a, 30, 5, torch, flush, True), c.kv_bytes)
+    capture(f"{name}.dynamic", c, r.out, r.lse)
     entry["dynamic_three_launch"] = stats(per_step_flushed(r, a, 30, 5, torch, flush, False), c.kv_bytes)
     ms_b2b, _ = timed_fused(r, a, 30, 5, torch)
     entry["dynamic_us_back_to_back"] = us(ms_b2b)
@@ -280,6 +349,7 @@ def batch_leg(cid, torch, L, wl, W_of, flush, static_sweep=False):
             t = per_step_flushed(r, a, 20, 3, torch, flush, True)
             t3 = per_step_flushed(r, a, 20, 3, torch, flush, False)
             if S == 0:
+                capture(f"{name}.static_default", c, r.out, r.lse)
                 entry["static_default_splits"] = L.attn_static_splits(a.shape)
                 entry["static_default"] = stats(t, c.kv_bytes)
                 entry["static_default_three_launch"] = stats(t3, c.kv_bytes)
@@ -302,6 +372,7 @@ def batch_leg(cid, torch, L, wl, W_of, flush, static_sweep=False):
         rl = Runner(cl, torch, L, W)
         a = rl.attention(L.ATTN_DYNAMIC)
         t = per_step_flushed(rl, a, 20, 3, torch, flush, True)
+        capture(f"{name}.long_request_last.dynamic", cl, rl.out, rl.lse)
         del a
         a = rl.attention(L.ATTN_STATIC)
         ts = per_step_flushed(rl, a, 20, 3, torch, flush, True)
@@ -324,9 +395,11 @@ def tiny_leg(torch, L, wl, W_of, steps=200):
     r = Runner(c, torch, L, W)
     a = r.attention(L.ATTN_DYNAMIC)
     fused = bracketed_ahead(lambda: r.fused(a), steps, torch)
+    capture("tiny", c, r.out, r.lse)
     three = bracketed_ahead(lambda: r.three(a), steps, torch)
+    W_eff = r.w_eff(a)
     del a, r
-    return {"kv_mb": round(c.kv_bytes / 1e6, 3), "tokens": c.total_tokens, "num_wgs": W,
+    return {"kv_mb": round(c.kv_bytes / 1e6, 3), "tokens": c.total_tokens, "num_wgs": W_eff,
             "single_launch_us_per_step": us(fused), "three_launch_us_per_step": us(three),
             "single_launch_gbs": round(c.kv_bytes / (fused * 1e-3) / 1e9, 1)}
 
@@ -345,18 +418,22 @@ def shared_leg(torch, L, wl, W_of, flush, Hq):
     r = Runner(c, torch, L, W)
     per_tok = 2 * c.Hkv * c.D * c.elem_bytes
     entry = {"requests": c.B, "q_heads": Hq, "kv_heads": c.Hkv, "requests_per_shared_pass": max(1, (32 if c.G >= 8 else 16) // c.G),
-             "logical_gb": round(c.kv_bytes / 1e9, 4), "num_wgs": W}
+             "logical_gb": round(c.kv_bytes / 1e9, 4)}
     a = r.attention(L.ATTN_DYNAMIC)
     t_dyn = per_step_flushed(r, a, 30, 5, torch, flush, True)
     entry["dynamic"] = stats(t_dyn, c.kv_bytes)
+    capture_sample(f"shared_prefix_hq{Hq}.dynamic", c, r.out, r.lse, [0, 1, 5, 30, 63])
     del a
     a = r.attention(L.ATTN_SHARED)
     r.plan(a)
+    torch.cuda.synchronize()
     p = a.read_plan()
+    entry["num_wgs"] = int(p["header"][2])
     read = int(np.asarray(p["len_eff"], np.int64).sum()) * per_tok
     entry["shared_items"] = int((np.asarray(p["item_m"]) > 1).sum())
     entry["read_gb"] = round(read / 1e9, 4)
     t_sh = per_step_flushed(r, a, 30, 5, torch, flush, True)
+    capture_sample(f"shared_prefix_hq{Hq}.shared", c, r.out, r.lse, [0, 1, 2, 3, 17, 30, 45, 63])
     med = float(np.median(t_sh))
     entry["shared"] = {"us_median": us(med), "us_p10": us(np.percentile(t_sh, 10)),
                        "us_p90": us(np.percentile(t_sh, 90)),
@@ -468,7 +545,9 @@ def trace_leg(torch, L, W_of, flush, steps=256):
     with torch.cuda.graph(graph):
         fused()
     torch.cuda.synchronize()
-    tf, t3, tg, kvb, host_eager, host_graph = [], [], [], [], [], []
+    tf, t3, tg, kvb, host_eager, host_graph, weff = [], [], [], [], [], [], []
+    check_at = {0, steps // 2, steps - 1}
+    rng = np.random.default_rng(0)
     while True:
         flush.sum()
         a, b = ev(torch), ev(torch)
@@ -479,6 +558,12 @@ def trace_leg(torch, L, W_of, flush, steps=256):
         b.record()
         torch.cuda.synchronize()
         tf.append(a.elapsed_time(b))
+        if dt.step in check_at:
+            # sampled requests (the longest, those just replaced, and random ones)
+            ids = set(rng.choice(tr.slots, 8, replace=False).tolist()) | {int(np.argmax(tr.lengths))}
+            if dt.step > 0:
+                ids |= {slot for slot, _ in tr.events[dt.step - 1]}
+            capture_sample(f"trace_fp8.step{dt.step}", tr.case(), out, lse, ids)
         flush.sum()
         a, b = ev(torch), ev(torch)
         a.record()
@@ -493,6 +578,7 @@ def trace_leg(torch, L, W_of, flush, steps=256):
         three(evs)
         torch.cuda.synchronize()
         t3.append([evs[j].elapsed_time(evs[j + 1]) for j in range(3)])
+        weff.append(int(att.read_plan()["header"][2]))
         kvb.append(2 * tr.Hkv * tr.D * int(np.asarray(tr.lengths, np.int64).sum()))
         if dt.step == steps - 1:
             break
@@ -514,7 +600,8 @@ def trace_leg(torch, L, W_of, flush, steps=256):
                 "us_per_step_mean": round(float(t.mean()), 2),
                 "effective_gbs": round(gbs, 2), "pct_hbm": round(100 * gbs / HBM_PEAK_GBS, 2)}
 
-    out_d = {"steps": steps, "num_wgs": W, "kv_gb_mean": round(float(kvb.mean()) / 1e9, 4),
+    out_d = {"steps": steps, "num_wgs": {"min": min(weff), "max": max(weff)},
+             "kv_gb_mean": round(float(kvb.mean()) / 1e9, 4),
              "single_launch": summary(tf),
              "single_launch_graph_replay": summary(tg),
              "host_issue_us_median": {"single_launch_eager": round(float(np.median(host_eager)) * 1e6, 2),
@@ -595,13 +682,106 @@ def traffic_entry(kernel):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
+def kernel_stats_entry(kernel):
+    """Average duration (ns) of `kernel` in the committed rocprofv3 kernel
+    trace of the headline command, only if taken on the current kernel source."""
+    if not os.path.exists(KERNEL_STATS_FILE):
+        return None
+    with open(KERNEL_STATS_FILE) as f:
+        t = json.load(f)
+    if t.get("source_hash") != source_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("avg_ns")
+
+
+def _short_name(name):
+    """'vlkv::(anonymous namespace)::decode_kernel<2, 0>(vlkv::DecodeArgs)' -> 'decode_kernel<2, 0>'."""
+    n = name.split("(")[0] if "(anonymous" not in name else name.replace("(anonymous namespace)", "")
+    n = n.split("(")[0]
+    return n.split("::")[-1].strip()
+
+
+def write_kernel_stats(d, out_json):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {d}")
+    kernels = {}
+    for row in csv.DictReader(open(files[0])):
+        kernels[_short_name(row["Name"])] = {"calls": int(row["Calls"]), "avg_ns": float(row["AverageNs"]),
+                                             "min_ns": float(row["MinNs"]), "max_ns": float(row["MaxNs"])}
+    res = {"source_hash": source_hash(), "stats_file": os.path.basename(files[0]), "kernels": kernels}
+    with open(out_json, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res, indent=1))
+
+
+def write_traffic_summary(fetch_dir, write_dir, probe_output, out_json):
+    """HBM bytes per launch from the FETCH_SIZE and WRITE_SIZE counters (KiB
+    per dispatch), each scaled by what it reads for the plain 1 GiB copy that
+    --traffic-probe runs first."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    def per_dispatch(d, counter):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        vals, names = defaultdict(float), {}
+        for fn in files:
+            for row in csv.DictReader(open(fn)):
+                if row["Counter_Name"] != counter:
+                    continue
+                key = (fn, int(row["Dispatch_Id"]))
+                vals[key] += float(row["Counter_Value"])
+                names[key] = _short_name(row["Kernel_Name"])
+        out = defaultdict(list)
+        for k in sorted(vals, key=lambda kk: kk[1]):
+            out[names[k]].append(vals[k])
+        return out
+
+    def pick(d, sub):
+        ks = [k for k in d if sub in k]
+        if len(ks) != 1:
+            raise SystemExit(f"kernel {sub!r}: found {ks}")
+        return d[ks[0]]
+
+    fetch = per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = per_dispatch(write_dir, "WRITE_SIZE")
+    probe = json.loads([ln for ln in open(probe_output) if ln.startswith("{")][-1])
+    copy_bytes = probe["copy_bytes"]
+    big = lambda v: [x for x in v if x > copy_bytes / 1024 / 4]   # the 1 GiB copies only
+    cf = float(np.mean(big(pick(fetch, "copyBuffer"))))
+    cw = float(np.mean(big(pick(write, "copyBuffer"))))
+    fs, ws = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    alg = probe["decode_kv_bytes"]
+    res = {"workload": "uniform-mixed, 32 requests, 284965 tokens (headline step)",
+           "source_hash": probe["source_hash"], "copy_fetch_kib": round(cf, 1), "copy_write_kib": round(cw, 1),
+           "fetch_scale": round(fs, 5), "write_scale": round(ws, 5), "algorithmic_bytes_per_launch": alg,
+           "kernels": {}}
+    for k in (FUSED_KERNEL, THREE_KERNEL, "plan_kernel", "combine_kernel"):
+        f, w = pick(fetch, k), pick(write, k)
+        fk, wk = float(np.mean(f)), float(np.mean(w))
+        rb, wb = round(fk * 1024 * fs), round(wk * 1024 * ws)
+        res["kernels"][k] = {"launches": len(f), "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+                             "hbm_read_bytes_per_launch": rb, "hbm_write_bytes_per_launch": wb,
+                             "hbm_bytes_per_launch": rb + wb, "read_over_algorithmic": round(rb / alg, 4),
+                             "spread_fetch_kib": [round(min(f), 1), round(max(f), 1)]}
+    with open(out_json, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--wgs-per-cu", type=int, default=0,
-                    help="workgroups per CU of the dynamic plan (0: the library's suggestion per workload)")
+                    help="workgroups per CU of the launches (0: the library's default)")
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--extra-legs", default="tiny,skewed,long_tail,trace,shared,router",
                     help="comma list of the extra workloads to run (tiny, skewed, long_tail, trace, shared, router)")
@@ -613,7 +793,17 @@ def main():
                     help="only the launches that the rocprofv3 --pmc runs measure")
     ap.add_argument("--router-probe", action="store_true",
                     help="only the router GEMM launches that its rocprofv3 runs measure")
+    ap.add_argument("--kernel-stats", nargs=2, metavar=("ROCPROF_DIR", "OUT_JSON"),
+                    help="summarise a rocprofv3 --kernel-trace --stats run (no GPU work)")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "PROBE_OUTPUT", "OUT_JSON"),
+                    help="summarise the FETCH_SIZE and WRITE_SIZE rocprofv3 --pmc runs of --traffic-probe")
     args = ap.parse_args()
+    if args.kernel_stats:
+        write_kernel_stats(*args.kernel_stats)
+        return
+    if args.traffic_summary:
+        write_traffic_summary(*args.traffic_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would run its own "
               "requests' plan independently); run it with --gpus 1.", file=sys.stderr)
@@ -627,7 +817,7 @@ def main():
     cus = L.attn_device_cu_count(0)
 
     def W_of(lengths, Hkv):
-        return pick_wgs(args, L, cus, lengths, Hkv)
+        return pick_wgs(args, cus)
 
     if args.traffic_probe:
         traffic_probe(torch, L, W_of(wl.config_lengths(1), 8))
@@ -641,21 +831,28 @@ def main():
     c1 = wl.config_case(1)
     log(f"bench: workload 1 generated in {time.perf_counter() - t0:.1f} s "
         f"({c1.kv_bytes / 1e9:.3f} GB of KV, {c1.total_tokens} tokens)")
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")   # 1 GiB read sweep
     W = W_of(c1.lengths, c1.Hkv)
     r1 = Runner(c1, torch, L, W)
     att = r1.attention(L.ATTN_DYNAMIC)
     n_settle = settle(r1, att, torch, args.settle_s)
     log(f"bench: {n_settle} untimed settling steps of each form ({args.settle_s} s)")
-    ms, per_f = timed_fused(r1, att, args.steps, args.warmup, torch)
+    ms_b2b, _ = timed_fused(r1, att, args.steps, args.warmup, torch)
     ms3, per3 = timed_three(r1, att, args.steps, args.warmup, torch)
-    launch_ms = float(per_f.mean())
+    # the headline: exactly K steps, each timed alone after the sweep
+    ts = per_step_flushed(r1, att, args.steps, args.warmup, torch, flush, True)
+    capture("uniform_mixed", c1, r1.out, r1.lse)
+    ms = float(np.median(ts))
+    launch_ms = float(ts.mean())
+    W_eff = r1.w_eff(att)
     plan_ms, dec_ms, comb_ms = per3.mean(axis=0)
-    log(f"bench: headline single launch {ms * 1e3:.1f} us/step (launch {launch_ms * 1e3:.1f}); three launches "
-        f"{ms3 * 1e3:.1f} us/step (plan {plan_ms * 1e3:.1f}, decode {dec_ms * 1e3:.1f}, "
-        f"combine {comb_ms * 1e3:.1f})")
+    log(f"bench: headline single launch {ms * 1e3:.1f} us/step flushed (mean {launch_ms * 1e3:.1f}), "
+        f"{ms_b2b * 1e3:.1f} back to back; three launches {ms3 * 1e3:.1f} us/step back to back (plan "
+        f"{plan_ms * 1e3:.1f}, decode {dec_ms * 1e3:.1f}, combine {comb_ms * 1e3:.1f})")
     kv = c1.kv_bytes
     value = kv / (ms * 1e-3) / 1e9
     achieved = kv / (launch_ms * 1e-3) / 1e9
+    rp = kernel_stats_entry(FUSED_KERNEL)
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -673,9 +870,13 @@ def main():
                                "64 q / 8 kv heads, head_dim 128, bf16 KV, page 64, random page table",
                    "global_batch": c1.B, "seq_len": int(c1.lengths.max()), "parallelism": "single GPU",
                    "step": "attn_step: tile plan + split-KV decode + LSE merge in one launch",
-                   "tile_tokens": 64, "num_wgs": W, "settle_s": args.settle_s, "us_per_step": us(ms),
+                   "timing": "median of K steps, each between HIP events after a 1 GiB read sweep",
+                   "tile_tokens": 64, "num_wgs": W_eff, "settle_s": args.settle_s, "us_per_step": us(ms),
+                   "us_per_step_p10": us(np.percentile(ts, 10)), "us_per_step_p90": us(np.percentile(ts, 90)),
                    "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-                   "three_launch": {"us_per_step": us(ms3),
+                   "us_per_step_back_to_back": us(ms_b2b),
+                   "pct_hbm_peak_back_to_back": round(100 * kv / (ms_b2b * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                   "three_launch": {"us_per_step_back_to_back": us(ms3),
                                     "pct_hbm_peak": round(100 * kv / (ms3 * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
                                     "plan_us": us(plan_ms), "decode_us": us(dec_ms), "combine_us": us(comb_ms),
                                     "decode_kernel_pct_hbm": round(100 * kv / (dec_ms * 1e-3) / 1e9
@@ -683,7 +884,13 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_entry(FUSED_KERNEL),
                      "kernel": FUSED_KERNEL + " (single launch, dynamic plan, bf16 KV)",
-                     "algorithmic_bytes_per_launch": kv, "launch_avg_us": us(launch_ms)},
+                     "algorithmic_bytes_per_launch": kv, "launch_avg_us": us(launch_ms),
+                     "launch_timing": "HIP events around each launch on the library's stream, after a 1 GiB "
+                                      "sweep (dispatch included)",
+                     "rocprof": None if rp is None else {
+                         "avg_us": round(rp / 1e3, 2),
+                         "frac": round(kv / (rp * 1e-9) / 1e9 / HBM_PEAK_GBS, 4),
+                         "source": os.path.relpath(KERNEL_STATS_FILE, ROOT)}},
     }
     del att, r1
     torch.cuda.empty_cache()
@@ -692,7 +899,6 @@ def main():
     if not args.no_extra:
         extra = {}
         legs = set(args.extra_legs.split(","))
-        flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
         if "tiny" in legs:
             extra["tiny"] = tiny_leg(torch, L, wl, W_of)
             log(f"bench: tiny: {json.dumps(extra['tiny'])}")
@@ -713,15 +919,22 @@ def main():
         if "router" in legs:
             extra["router_gemm"] = router_leg(torch, L)
             log(f"bench: router_gemm: {json.dumps(extra['router_gemm'])}")
-        del flush
-        torch.cuda.empty_cache()
         result["extra"] = extra
+    del flush
+    torch.cuda.empty_cache()
 
-    # ---- CPU baseline (the oracle on the headline workload) -------------------
+    # ---- CPU baseline (the oracle on the headline workload) and parity --------
+    ok = True
     if args.cpu_budget > 0:
-        result["cpu_baseline"] = cpu_baseline(c1, args.cpu_budget)
+        result["cpu_baseline"], parity = cpu_baseline(c1, args.cpu_budget, CAPTURES)
+        ok = all(v["ok"] for v in parity.values())
+        result["parity"] = {"ok": ok, "reference": "CPU fp64 oracle", "checks": parity}
         log(f"bench: cpu baseline {result['cpu_baseline']}")
+        log(f"bench: parity {'ok' if ok else 'FAILED'}: " + ", ".join(
+            f"{k} {v['worst_err_over_bound']}" for k, v in parity.items()))
     print(json.dumps(result), flush=True)
+    if not ok:
+        sys.exit(1)
 
 
 if __name__ == "__main__":

@@ -80,12 +80,18 @@ extern "C" {
  *   num_pages      physical pages in each cache
  *   pt_stride      row length of the page table (max pages per request)
  *   tile_tokens    T, the uniform tile; a multiple of 64
- *   num_wgs        W, workgroups of the dynamic decode launch (>= 1); a good
- *                  value is 2 per compute unit (attn_device_cu_count)
+ *   num_wgs        W, workgroups of the decode launch (>= 1), or 0 for the
+ *                  library default: a launch of 2 per compute unit of the
+ *                  current device, of which the dynamic plan uses all when
+ *                  that leaves at least 32 units (request, kv head, tile) per
+ *                  workgroup, else one per compute unit (the fixed costs of a
+ *                  workgroup outweigh a second wave per SIMD on small steps).
+ *                  With 0, sizes and splits below follow the current device.
  *   kv_dtype       ATTN_KV_BF16 or ATTN_KV_FP8_E4M3
  *   mode           ATTN_DYNAMIC, ATTN_STATIC or ATTN_SHARED
  *   static_splits  S for ATTN_STATIC (>= 1); 0 picks
- *                  clamp(ceil(num_wgs / (B*Hkv)), 1, ceil(pt_stride*P / T))
+ *                  clamp(ceil(W / (B*Hkv)), 1, ceil(pt_stride*P / T)) with
+ *                  W = attn_num_wgs(shape)
  */
 typedef struct attn_shape {
     int32_t batch;
@@ -110,13 +116,22 @@ int attn_check_shape(const attn_shape *shape);
 
 /*
  * Bytes of workspace the three calls need for this shape, for any lengths
- * within pt_stride * page_size. Host only, pure. Returns 0 for an invalid
- * shape. The workspace must be device memory aligned to 256 bytes.
+ * within pt_stride * page_size. Host only, pure (with num_wgs = 0 it reads the
+ * current device's compute-unit count). Returns 0 for an invalid shape. The
+ * workspace must be device memory aligned to 256 bytes.
  */
 size_t attn_workspace_bytes(const attn_shape *shape);
 
 /* Effective number of static splits S for this shape (ATTN_STATIC), or 0. */
 int32_t attn_static_splits(const attn_shape *shape);
+
+/*
+ * Workgroups the decode launch of this shape has: num_wgs, or for num_wgs = 0
+ * two per compute unit of the current device (the size of the plan's
+ * per-workgroup arrays, attn_read_plan). 0 for an invalid shape or, with
+ * num_wgs = 0, when no device is available.
+ */
+int32_t attn_num_wgs(const attn_shape *shape);
 
 /*
  * Number of compute units of HIP device `device` in *cus (host pointer).
@@ -130,7 +145,8 @@ int attn_device_cu_count(int device, int32_t *cus);
  *   page_table (device) int32 [B][pt_stride]; read only in ATTN_SHARED mode
  *   workspace  (device) >= attn_workspace_bytes(shape) bytes, 256-B aligned
  * Dynamic mode: the (request, kv head, tile) units are numbered request-major
- * and cut into num_wgs contiguous, equal (+-1) ranges; each maximal run of one
+ * and cut into W_eff contiguous, equal (+-1) ranges (W_eff: the workgroups the
+ * plan uses, see num_wgs, and at most the number of units); each maximal run of one
  * (request, kv head) inside a range is a segment with its own partial slot.
  * Static mode: chunk = ceil(max L / S) rounded up to a multiple of
  * lcm(page_size, tile_tokens); split s of each (request, kv head) covers
@@ -232,7 +248,7 @@ int attn_step(const attn_shape *shape, const void *q, const void *k_cache, const
  *           it (the caller clears it); NULL keeps them in the scratch, unread.
  * Limits, checked on the host (ATTN_ERR_INVALID_ARG, nothing enqueued):
  * batch * num_kv_heads <= ATTN_NOALLOC_MAX_PAIRS, and the partial results must
- * fit the scratch: 2 * num_wgs slots (ATTN_DYNAMIC) or batch * num_kv_heads * S
+ * fit the scratch: 2 * W slots (ATTN_DYNAMIC, W = attn_num_wgs) or batch * num_kv_heads * S
  * slots (ATTN_STATIC), each Hq/Hkv rows of head_dim + 1 floats, plus 256 bytes
  * of alignment, at most ATTN_NOALLOC_SCRATCH_BYTES - 4 * ATTN_NOALLOC_MAX_PAIRS
  * - 256 bytes. ATTN_SHARED returns ATTN_ERR_UNSUPPORTED (its plan needs a
@@ -287,7 +303,7 @@ int attn_get_status(const void *workspace, uint32_t *flags, void *stream);
  * Copy the plan arrays out of the workspace into host memory (synchronises
  * `stream`), for checking the device planner against a CPU planner. Each host
  * pointer may be NULL to skip that array. Sizes: header[8], len_eff[B],
- * tiles_prefix[B+1], seg_prefix[B*Hkv+1], first_wg[B*Hkv], wg_begin[W+1],
+ * tiles_prefix[B+1], seg_prefix[B*Hkv+1], first_wg[B*Hkv], wg_begin[W+1] (W = attn_num_wgs),
  * wg_start_b[W]. header = {status, N, W_eff, max L, chunk, S, total tiles, T}.
  * ATTN_SHARED: the arrays are over items, not requests, with B replaced by 2B
  * (the first header[4] items are used): len_eff = item token counts,

@@ -41,9 +41,9 @@ def _load():
         lib.oracle_decode.restype = i32
         lib.oracle_decode.argtypes = [i32] * 8 + [P] * 7 + [ctypes.c_double, P, i32, P, P, i32]
         lib.oracle_plan.restype = i32
-        lib.oracle_plan.argtypes = [i32] * 8 + [P] * 8
+        lib.oracle_plan.argtypes = [i32] * 9 + [P] * 8
         lib.oracle_plan_shared.restype = i32
-        lib.oracle_plan_shared.argtypes = [i32] * 8 + [P] * 16
+        lib.oracle_plan_shared.argtypes = [i32] * 9 + [P] * 16
         lib.oracle_bf16_rne.restype = ctypes.c_uint16
         lib.oracle_bf16_rne.argtypes = [ctypes.c_float]
         lib.oracle_router_split.restype = None
@@ -159,8 +159,10 @@ def decode(case, req_ids=None, threads=0, *, lengths=None, page_table=None, sm_s
     return out, lse
 
 
-def plan(mode, lengths, Hkv, P, pt_stride, T, W, S=0):
-    """Integer tile plan (mode 0 dynamic, 1 static). Returns a dict of int32 arrays."""
+def plan(mode, lengths, Hkv, P, pt_stride, T, W, S=0, cus=0):
+    """Integer tile plan (mode 0 dynamic, 1 static). Returns a dict of int32
+    arrays. ``cus`` > 0 selects the library's default workgroup count (then
+    W = 2 * cus): W when that leaves at least 32 units per workgroup, else cus."""
     lib = _load()
     lengths = _np(lengths, np.int32)
     B = len(lengths)
@@ -173,7 +175,7 @@ def plan(mode, lengths, Hkv, P, pt_stride, T, W, S=0):
         "wg_begin": np.zeros(W + 1, np.int32),
         "wg_start_b": np.zeros(W, np.int32),
     }
-    rc = lib.oracle_plan(int(mode), B, Hkv, P, pt_stride, T, W, int(S), _ptr(lengths),
+    rc = lib.oracle_plan(int(mode), B, Hkv, P, pt_stride, T, W, int(S), int(cus), _ptr(lengths),
                          *[_ptr(out[k]) for k in ("header", "len_eff", "tiles_prefix", "seg_prefix",
                                                   "first_wg", "wg_begin", "wg_start_b")])
     if rc != 0:
@@ -181,7 +183,7 @@ def plan(mode, lengths, Hkv, P, pt_stride, T, W, S=0):
     return out
 
 
-def plan_shared(lengths, page_table, Hkv, G, P, num_pages, T, W):
+def plan_shared(lengths, page_table, Hkv, G, P, num_pages, T, W, cus=0):
     """Integer plan with prefix-shared pages (mode 2). Returns a dict of int32
     arrays; the item arrays are cut to the number of items."""
     lib = _load()
@@ -205,7 +207,7 @@ def plan_shared(lengths, page_table, Hkv, G, P, num_pages, T, W):
     }
     keys = ("header", "item_req", "item_start", "item_len", "item_m", "item_solo", "req_shared", "req_member",
             "req_own", "tiles_prefix", "seg_prefix", "first_wg", "wg_begin", "wg_start")
-    rc = lib.oracle_plan_shared(B, Hkv, G, P, pt_stride, num_pages, T, W, _ptr(lengths), _ptr(pt),
+    rc = lib.oracle_plan_shared(B, Hkv, G, P, pt_stride, num_pages, T, W, int(cus), _ptr(lengths), _ptr(pt),
                                 *[_ptr(out[k]) for k in keys])
     if rc != 0:
         raise ValueError(f"oracle_plan_shared failed with code {rc}")

@@ -216,7 +216,12 @@ int oracle_decode(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
  * bit 1 is set. A unit is (b, g, t) with g < Hkv, t < n_b, numbered in the order
  * b, then g, then t; N = Hkv * sum_b n_b units in all.
  *
- * Dynamic mode (mode 0). With W workgroups, W_eff = min(W, N). Workgroup w owns
+ * Workgroup count. W is given, or chosen by the library default: with cus > 0
+ * (the device's compute units; then W must be 2*cus) the plan uses W_use = W
+ * when that leaves at least 32 units per workgroup (N >= 32*W) and W_use = cus
+ * otherwise; with cus = 0, W_use = W. The arrays below still span W.
+ *
+ * Dynamic mode (mode 0). With W_use workgroups, W_eff = min(W_use, N). Workgroup w owns
  * the contiguous unit range [floor(w*N/W_eff), floor((w+1)*N/W_eff)), so no two
  * workgroups differ by more than one unit. Unit u's owner is
  * floor(((u+1)*W_eff - 1) / N). A segment is a maximal run of one (b, g) inside
@@ -250,14 +255,23 @@ static int64_t gcd64(int64_t a, int64_t b)
     return a;
 }
 
+/* The workgroups a dynamic plan of N units uses (see "Workgroup count"). */
+static int64_t wgs_used(int64_t N, int32_t W, int32_t cus)
+{
+    if (cus > 0 && N < (int64_t)32 * W)
+        return cus;
+    return W;
+}
+
 int oracle_plan(int32_t mode, int32_t B, int32_t Hkv, int32_t P, int32_t pt_stride,
-                int32_t T, int32_t W, int32_t S, const int32_t *lengths,
+                int32_t T, int32_t W, int32_t S, int32_t cus, const int32_t *lengths,
                 int32_t *header, int32_t *len_eff, int32_t *tiles_prefix,
                 int32_t *seg_prefix, int32_t *first_wg, int32_t *wg_begin,
                 int32_t *wg_start_b)
 {
     if (B < 0 || Hkv <= 0 || P <= 0 || pt_stride < 0 || T <= 0 || W <= 0 ||
-        (mode != 0 && mode != 1) || (mode == 1 && S <= 0))
+        (mode != 0 && mode != 1) || (mode == 1 && S <= 0) || cus < 0 ||
+        (cus > 0 && W != 2 * cus))
         return ORACLE_EINVAL;
     int32_t status = 0;
     int64_t total = 0, maxle = 0;
@@ -299,7 +313,8 @@ int oracle_plan(int32_t mode, int32_t B, int32_t Hkv, int32_t P, int32_t pt_stri
     const int64_t N = total * Hkv;
     if (N > INT32_MAX)
         return -4;
-    const int64_t We = N < W ? N : W;
+    const int64_t Wu = wgs_used(N, W, cus);
+    const int64_t We = N < Wu ? N : Wu;
     int64_t nseg = 0;
     seg_prefix[0] = 0;
     for (int32_t b = 0; b < B; ++b) {
@@ -378,13 +393,15 @@ int oracle_plan(int32_t mode, int32_t B, int32_t Hkv, int32_t P, int32_t pt_stri
  * 2B*Hkv+1; first_wg 2B*Hkv; wg_begin W+1; wg_start W.
  */
 int oracle_plan_shared(int32_t B, int32_t Hkv, int32_t G, int32_t P, int32_t pt_stride, int32_t num_pages,
-                       int32_t T, int32_t W, const int32_t *lengths, const int32_t *page_table, int32_t *header,
+                       int32_t T, int32_t W, int32_t cus, const int32_t *lengths, const int32_t *page_table,
+                       int32_t *header,
                        int32_t *item_req, int32_t *item_start, int32_t *item_len, int32_t *item_m,
                        int32_t *item_solo, int32_t *req_shared, int32_t *req_member, int32_t *req_own,
                        int32_t *tiles_prefix, int32_t *seg_prefix, int32_t *first_wg, int32_t *wg_begin,
                        int32_t *wg_start)
 {
-    if (B < 0 || Hkv <= 0 || G <= 0 || P <= 0 || pt_stride < 0 || num_pages <= 0 || T <= 0 || W <= 0)
+    if (B < 0 || Hkv <= 0 || G <= 0 || P <= 0 || pt_stride < 0 || num_pages <= 0 || T <= 0 || W <= 0 ||
+        cus < 0 || (cus > 0 && W != 2 * cus))
         return ORACLE_EINVAL;
     const int32_t R = G >= 32 ? 1 : G >= 8 ? 32 / G : 16 / G;
     int32_t status = 0;
@@ -480,7 +497,8 @@ int oracle_plan_shared(int32_t B, int32_t Hkv, int32_t G, int32_t P, int32_t pt_
     const int64_t N = total * Hkv;
     if (N > INT32_MAX)
         return -4;
-    const int64_t We = N < W ? N : W;
+    const int64_t Wu = wgs_used(N, W, cus);
+    const int64_t We = N < Wu ? N : Wu;
     int64_t nseg = 0;
     seg_prefix[0] = 0;
     for (int64_t i = 0; i < I; ++i) {

@@ -62,7 +62,7 @@ def test_default_static_splits():
     (dict(page_size=8), L.ATTN_ERR_INVALID_ARG),
     (dict(page_size=24), L.ATTN_ERR_INVALID_ARG),
     (dict(tile_tokens=32), L.ATTN_ERR_UNSUPPORTED),
-    (dict(num_wgs=0), L.ATTN_ERR_INVALID_ARG),
+    (dict(num_wgs=-1), L.ATTN_ERR_INVALID_ARG),
     (dict(kv_dtype=7), L.ATTN_ERR_UNSUPPORTED),
     (dict(mode=3), L.ATTN_ERR_INVALID_ARG),
     (dict(num_pages=0), L.ATTN_ERR_INVALID_ARG),
@@ -102,13 +102,21 @@ def test_null_arguments_rejected_before_launch():
     assert lib.attn_get_status(None, None, None) == L.ATTN_ERR_INVALID_ARG
 
 
-def test_suggested_workgroup_count():
-    # two per compute unit unless that leaves fewer than 32 tiles per workgroup
-    assert L.suggest_num_wgs(256, [16000] + [1000] * 63, 8) == 256     # 10,064 tiles
-    assert L.suggest_num_wgs(256, [8900] * 32, 8) == 512               # 35,840 tiles
-    assert L.suggest_num_wgs(4, [0, -5], 1) == 4
-    assert L.suggest_num_wgs(2, [64 * 32 * 4], 1) == 4                 # exactly 32 tiles per workgroup
-    assert L.suggest_num_wgs(2, [64 * 32 * 4 - 64], 1) == 2
+def test_default_workgroup_count_is_the_librarys():
+    # num_wgs = 0 is a valid shape (the library's default, resolved on the
+    # device at call time); the binding does no plan arithmetic of its own
+    s = _shape(num_wgs=0)
+    L.attn_check_shape(s)
+    assert not hasattr(L, "suggest_num_wgs")
+    lib = L.load()
+    assert lib.attn_num_wgs(ctypes.byref(_shape(num_wgs=300).c())) == 300
+    assert lib.attn_num_wgs(ctypes.byref(_shape(num_wgs=-2).c())) == 0
+    import torch
+    if not torch.cuda.is_available():
+        # without a device the default cannot be resolved: sizes are refused
+        assert lib.attn_num_wgs(ctypes.byref(s.c())) == 0
+        assert lib.attn_workspace_bytes(ctypes.byref(s.c())) == 0
+        assert lib.attn_static_splits(ctypes.byref(_shape(num_wgs=0, mode=L.ATTN_STATIC).c())) == 0
 
 
 def test_append_rejects_bad_arguments_before_launch():

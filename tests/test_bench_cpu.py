@@ -54,3 +54,47 @@ def test_traffic_counters_follow_the_kernel_source():
         assert 1.0 <= t["kernels"][bench.FUSED_KERNEL]["read_over_algorithmic"] < 1.05
     else:
         assert entry is None
+
+
+def test_compare_flags_out_of_bound_outputs():
+    import numpy as np
+    import torch
+    rng = np.random.default_rng(0)
+    ref = rng.standard_normal((3, 4, 128)) * 0.05
+    ref_l = rng.standard_normal((3, 4))
+    ref_l[1] = -np.inf                       # an empty request
+    out = torch.tensor(ref).to(torch.bfloat16)
+    lse = torch.tensor(ref_l, dtype=torch.float32)
+    good = bench.compare(out, lse, ref, ref_l, "bf16")
+    assert good["ok"] and good["worst_err_over_bound"] < 0.1
+    bad = out.clone()
+    bad[2, 1, 7] += 0.5                      # one element off by far more than the bound
+    assert not bench.compare(bad, lse, ref, ref_l, "bf16")["ok"]
+    nan = out.clone()
+    nan[0, 0, 0] = float("nan")
+    assert not bench.compare(nan, lse, ref, ref_l, "bf16")["ok"]
+    lbad = lse.clone()
+    lbad[0, 0] += 0.01
+    assert not bench.compare(out, lbad, ref, ref_l, "bf16")["ok"]
+    lfin = lse.clone()
+    lfin[1, 0] = 0.0                         # a finite lse where the reference has none
+    assert not bench.compare(out, lfin, ref, ref_l, "bf16")["ok"]
+
+
+def test_profile_kernel_names():
+    assert bench._short_name("vlkv::(anonymous namespace)::decode_kernel<2, 0>(vlkv::DecodeArgs)") == \
+        "decode_kernel<2, 0>"
+    assert bench._short_name("vlkv::(anonymous namespace)::plan_kernel(vlkv::PlanArgs)") == "plan_kernel"
+    assert bench._short_name("__amd_rocclr_copyBuffer") == "__amd_rocclr_copyBuffer"
+
+
+def test_kernel_stats_follow_the_kernel_source():
+    if not os.path.exists(bench.KERNEL_STATS_FILE):
+        return
+    with open(bench.KERNEL_STATS_FILE) as f:
+        t = json.load(f)
+    avg = bench.kernel_stats_entry(bench.FUSED_KERNEL)
+    if t["source_hash"] == bench.source_hash():
+        assert avg == t["kernels"][bench.FUSED_KERNEL]["avg_ns"]
+    else:
+        assert avg is None

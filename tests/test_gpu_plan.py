@@ -30,7 +30,11 @@ def _device_plan(lengths, Hkv, P, pt_stride, T, W, mode, S=0):
 
 def _compare(lengths, Hkv, P, pt_stride, T, W, mode, S=0):
     got, S_eff = _device_plan(lengths, Hkv, P, pt_stride, T, W, mode, S)
-    ref = oracle.plan(mode, lengths, Hkv, P, pt_stride, T, W, S_eff)
+    if W == 0:   # the library default: two per compute unit, or one on small steps
+        cus = L.attn_device_cu_count(0)
+        ref = oracle.plan(mode, lengths, Hkv, P, pt_stride, T, 2 * cus, S_eff, cus=cus if mode == 0 else 0)
+    else:
+        ref = oracle.plan(mode, lengths, Hkv, P, pt_stride, T, W, S_eff)
     keys = ["header", "len_eff", "tiles_prefix", "seg_prefix", "first_wg"]
     if mode == L.ATTN_DYNAMIC:
         keys += ["wg_begin", "wg_start_b"]
@@ -44,7 +48,7 @@ def test_workload_plans(cid, mode):
     lengths = wl.config_lengths(cid)
     Hkv, P = (1, 16) if cid == 0 else (8, 64)
     stride = int(-(-lengths.max() // P)) + 1
-    for W in (1, 256, 512, 2048):
+    for W in (0, 1, 256, 512, 2048):
         _compare(lengths, Hkv, P, stride, 64, W, mode)
 
 
@@ -64,6 +68,6 @@ def test_random_plans():
         stride = int(rng.integers(1, 300))
         lengths = rng.integers(-3, stride * P + 20, B) * (rng.random(B) < 0.9)
         Hkv = int(rng.choice([1, 2, 8]))
-        W = int(rng.choice([1, 3, 512, 4096]))
+        W = int(rng.choice([0, 1, 3, 512, 4096]))
         mode = int(rng.integers(2))
         _compare(lengths, Hkv, P, stride, T, W, mode, int(rng.integers(0, 5)))

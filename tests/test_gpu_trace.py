@@ -19,7 +19,7 @@ from variable_length_kv_amd import lib as L
 from variable_length_kv_amd import workloads as wl
 from variable_length_kv_amd.trace import DeviceTrace
 
-from gpu_helpers import FP8_TOL, check_close, num_cus
+from gpu_helpers import FP8_TOL, check_close
 
 pytestmark = pytest.mark.gpu
 
@@ -31,28 +31,45 @@ def _shape(tr, W):
 
 
 def _walk(tr, W, check_step, sample):
+    """Every step: the three launches (plan bit-exact against the CPU plan) and
+    the single launch attn_step, bitwise equal to them; at checked steps the
+    sampled requests against the CPU reference. Freed pages and the rows past
+    each length hold the e4m3fn NaN code, so a read outside the live rows
+    shows as NaN."""
     dt = DeviceTrace(tr)
     att = L.Attention(_shape(tr, W), "cuda:0")
+    fused = L.Attention(_shape(tr, W), "cuda:0")
     out = torch.empty_like(dt.q)
+    out1 = torch.empty_like(dt.q)
     lse = torch.empty(tr.slots, tr.Hq, dtype=torch.float32, device="cuda:0")
+    lse1 = torch.empty_like(lse)
+    cus = L.attn_device_cu_count(0)
     checked = 0
     while True:
         s = dt.step
         out.fill_(float("nan"))
+        out1.fill_(float("nan"))
         att.step(dt.q, dt.k, dt.v, dt.pt, dt.len, 1.0 / np.sqrt(tr.D), out, lse, k_scale=dt.ks,
                  v_scale=dt.vs)
+        fused.fused_step(dt.q, dt.k, dt.v, dt.pt, dt.len, 1.0 / np.sqrt(tr.D), out1, lse1, k_scale=dt.ks,
+                         v_scale=dt.vs)
         torch.cuda.synchronize()
-        assert att.status() == 0, f"step {s}"
+        assert att.status() == 0 and fused.status() == 0, f"step {s}"
+        assert torch.equal(out.view(torch.int16), out1.view(torch.int16)), f"step {s}: single launch differs"
+        assert torch.equal(lse.view(torch.int32), lse1.view(torch.int32)), f"step {s}: single launch lse differs"
         got = att.read_plan()
-        ref = oracle.plan(L.ATTN_DYNAMIC, tr.lengths, tr.Hkv, tr.P, tr.pt_stride, 64, W)
+        if W == 0:
+            ref = oracle.plan(L.ATTN_DYNAMIC, tr.lengths, tr.Hkv, tr.P, tr.pt_stride, 64, 2 * cus, cus=cus)
+        else:
+            ref = oracle.plan(L.ATTN_DYNAMIC, tr.lengths, tr.Hkv, tr.P, tr.pt_stride, 64, W)
         for k in ("header", "len_eff", "tiles_prefix", "seg_prefix", "first_wg", "wg_begin", "wg_start_b"):
             assert np.array_equal(got[k], ref[k]), f"step {s}: plan array {k}"
         if check_step(s):
             ids = sample(s)
             case = tr.case()
             ref_o, ref_l = oracle.decode(case, ids)
-            o = out.double().cpu().numpy()[ids]
-            ls = lse.double().cpu().numpy()[ids]
+            o = out1.double().cpu().numpy()[ids]
+            ls = lse1.double().cpu().numpy()[ids]
             check_close(o, ls, ref_o, ref_l, FP8_TOL, what=f"trace step {s}")
             checked += 1
         if s == tr.steps - 1:
@@ -69,9 +86,11 @@ def test_small_trace_every_step_every_request():
 
 @pytest.mark.slow
 def test_full_trace_sampled():
-    """The 256-step, 96-slot trace at full size: plan checked every step,
-    outputs of sampled requests every 8th step and at every step right after
-    a replacement."""
+    """The 256-step, 96-slot trace at full size, as the benchmark times it
+    (single launch, fp8 cache, default workgroup count): plan checked every
+    step, single launch bitwise equal to the three launches every step,
+    sampled requests against the CPU reference every 8th step and at every
+    step right after a replacement."""
     tr = wl.Trace()
     replaced_at = {s + 1 for s, ev in enumerate(tr.events) if ev}
     rng = np.random.default_rng(0)
@@ -83,5 +102,6 @@ def test_full_trace_sampled():
         ids.add(int(np.argmax(tr.lengths)))
         return sorted(ids)
 
-    n = _walk(tr, W=2 * num_cus(), check_step=lambda s: s % 8 == 0 or s in replaced_at, sample=sample)
+    # the benchmark's launch configuration: the library's default workgroup count
+    n = _walk(tr, W=0, check_step=lambda s: s % 8 == 0 or s in replaced_at, sample=sample)
     assert n >= 32

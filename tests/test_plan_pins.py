@@ -168,3 +168,36 @@ def test_workload_plan_sizes():
         L = wl.config_lengths(cid)
         p = oracle.plan(0, L, hkv, 16 if cid == 0 else 64, 2048, 64, 512)
         assert p["header"][1] == len(_brute_units(L.tolist(), hkv, 64, 2048 * 64))
+
+
+@pytest.mark.parametrize("tiles,w_eff", [(255, 4), (256, 8), (1, 1), (3, 3), (4, 4), (5, 4), (4000, 8)])
+def test_default_workgroup_count_hand_worked(tiles, w_eff):
+    """The library default (num_wgs = 0) on a device of 4 compute units: W = 8
+    workgroups when that leaves at least 32 units each (N >= 256), else one per
+    compute unit (4), and never more than N. One request of `tiles` 64-token
+    tiles on one kv head has N = tiles units."""
+    p = oracle.plan(0, [64 * tiles], 1, 64, tiles, 64, 8, cus=4)
+    assert p["header"][1] == tiles and p["header"][2] == w_eff
+    assert p["wg_begin"].tolist() == [w * tiles // w_eff if w <= w_eff else tiles for w in range(9)]
+    with pytest.raises(ValueError):   # the default spans two workgroups per compute unit
+        oracle.plan(0, [64], 1, 64, 1, 64, 7, cus=4)
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_default_workgroup_count_equals_explicit(seed):
+    """With the default count the plan is the explicit plan for the count the
+    rule picks, with the arrays padded to 2 * cus workgroups."""
+    rng = np.random.default_rng(500 + seed)
+    B, P, T, pt_stride, lengths, Hkv, _ = _random_inputs(rng)
+    cus = int(rng.choice([1, 3, 8, 256]))
+    p = oracle.plan(0, lengths, Hkv, P, pt_stride, T, 2 * cus, cus=cus)
+    N = len(_brute_units(lengths.tolist(), Hkv, T, pt_stride * P))
+    W = 2 * cus if N >= 64 * cus else cus
+    q = oracle.plan(0, lengths, Hkv, P, pt_stride, T, W)
+    assert p["header"].tolist() == q["header"].tolist()
+    for k in ("len_eff", "tiles_prefix", "seg_prefix", "first_wg"):
+        assert np.array_equal(p[k], q[k]), k
+    assert p["wg_begin"][:W + 1].tolist() == q["wg_begin"].tolist()
+    assert all(x == N for x in p["wg_begin"][W + 1:])
+    assert p["wg_start_b"][:W].tolist() == q["wg_start_b"].tolist()
+    assert all(x == B for x in p["wg_start_b"][W:])

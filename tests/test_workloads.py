@@ -78,7 +78,7 @@ def test_trace_host_state_is_consistent():
 def test_device_mirror_tracks_the_host_trace():
     from variable_length_kv_amd.trace import DeviceTrace
     tr = _small_trace()
-    dt = DeviceTrace(tr, "cpu")
+    dt = DeviceTrace(tr, "cpu", poison=False)   # an exact copy (poisoning: test_trace_poison.py)
     assert dt.k.data_ptr() != tr.k_cache.data_ptr()
     for _ in range(tr.steps - 1):
         dt.advance()
@@ -87,3 +87,18 @@ def test_device_mirror_tracks_the_host_trace():
         assert np.array_equal(dt.pt.numpy(), tr.page_table)
         assert np.array_equal(dt.len.numpy(), tr.lengths)
         assert torch.equal(dt.q, tr.q)
+
+
+def test_sub_case_keeps_the_requests_step():
+    """A sub-batch of a step (its requests' pages renumbered and copied) gives
+    the CPU reference the same result for those requests as the whole step,
+    bit for bit, for a bf16 and an fp8 cache."""
+    import oracle
+    for kv in ("bf16", "fp8"):
+        c = wl.make_case("full", [33, 0, 500, 64, 130], Hq=8, Hkv=2, P=16, kv_dtype=kv, seed=4)
+        ids = [4, 0, 2, 1]
+        sub = wl.sub_case(c, ids)
+        assert sub.B == 4 and sub.num_pages == sum(-(-int(c.lengths[i]) // 16) for i in ids)
+        o1, l1 = oracle.decode(c, ids)
+        o2, l2 = oracle.decode(sub)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)

@@ -36,12 +36,33 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-static int32_t effective_splits(const attn_shape *s)
+// Compute units of the current device, read once per device.
+static int device_cus(int *cus)
+{
+    constexpr int kMaxDev = 64;
+    static int cache[kMaxDev];
+    static std::once_flag once[kMaxDev];
+    static hipError_t err[kMaxDev];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(ATTN_ERR_HIP, "num_wgs 0 needs a device: hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDev)
+        return fail(ATTN_ERR_INVALID_ARG, "device %d beyond the %d this library serves", dev, kMaxDev);
+    std::call_once(once[dev], [&] { err[dev] = hipDeviceGetAttribute(&cache[dev], hipDeviceAttributeMultiprocessorCount, dev); });
+    if (err[dev] != hipSuccess)
+        return fail(ATTN_ERR_HIP, "hipDeviceGetAttribute: %s", hipGetErrorString(err[dev]));
+    *cus = cache[dev];
+    return ATTN_OK;
+}
+
+// Static split count S for a launch of W workgroups.
+static int32_t effective_splits(const attn_shape *s, int64_t W)
 {
     if (s->static_splits > 0)
         return s->static_splits;
     const int64_t pairs = (int64_t)s->batch * s->num_kv_heads;
-    int64_t S = ceil_div(s->num_wgs, pairs);
+    int64_t S = ceil_div(W, pairs);
     const int64_t cap = ceil_div((int64_t)s->pt_stride * s->page_size, s->tile_tokens);
     if (S > cap)
         S = cap;
@@ -74,8 +95,8 @@ static int check(const attn_shape *s, Shape *out)
     if (s->tile_tokens < kBlockTokens || s->tile_tokens % kBlockTokens)
         return fail(ATTN_ERR_UNSUPPORTED, "tile_tokens %d must be a positive multiple of %d",
                     s->tile_tokens, kBlockTokens);
-    if (s->num_wgs < 1 || s->num_wgs > (1 << 20))
-        return fail(ATTN_ERR_INVALID_ARG, "num_wgs %d outside [1, 2^20]", s->num_wgs);
+    if (s->num_wgs < 0 || s->num_wgs > (1 << 20))
+        return fail(ATTN_ERR_INVALID_ARG, "num_wgs %d outside [0, 2^20]", s->num_wgs);
     if (s->kv_dtype != ATTN_KV_BF16 && s->kv_dtype != ATTN_KV_FP8_E4M3)
         return fail(ATTN_ERR_UNSUPPORTED, "kv_dtype %d", s->kv_dtype);
     if (s->mode != ATTN_DYNAMIC && s->mode != ATTN_STATIC && s->mode != ATTN_SHARED)
@@ -90,15 +111,30 @@ static int check(const attn_shape *s, Shape *out)
     const int64_t max_units = (int64_t)s->batch * s->num_kv_heads * (ceil_div(max_tokens, s->tile_tokens) + 1);
     if (max_units > INT32_MAX / 2)
         return fail(ATTN_ERR_INVALID_ARG, "batch * kv heads * tiles per request too large");
-    const int32_t S = s->mode == ATTN_STATIC ? effective_splits(s) : 0;
+    // num_wgs 0: the library default, two workgroups per compute unit of the
+    // current device (read only when the shape is resolved for a call)
+    int W = s->num_wgs, W_auto = 0;
+    if (W == 0) {
+        if (!out)
+            W = 2;   // any device has a compute unit: check the rest with the smallest count
+        else {
+            int cus = 0;
+            const int rc = device_cus(&cus);
+            if (rc != ATTN_OK)
+                return rc;
+            W = 2 * cus;
+            W_auto = cus;
+        }
+    }
+    const int32_t S = s->mode == ATTN_STATIC ? effective_splits(s, W) : 0;
     if (s->mode == ATTN_STATIC && (int64_t)s->batch * s->num_kv_heads * S > INT32_MAX / 2)
         return fail(ATTN_ERR_INVALID_ARG, "batch * kv heads * splits too large");
     if (s->mode == ATTN_STATIC && (int64_t)S * max_tokens > ((int64_t)INT32_MAX) * 4)
         return fail(ATTN_ERR_INVALID_ARG, "static splits too large");
     if (out) {
         *out = Shape{s->batch, s->num_q_heads, s->num_kv_heads, G, s->head_dim, s->page_size,
-                     s->num_pages, s->pt_stride, s->tile_tokens, s->num_wgs,
-                     s->kv_dtype == ATTN_KV_FP8_E4M3, s->mode, S};
+                     s->num_pages, s->pt_stride, s->tile_tokens, W,
+                     s->kv_dtype == ATTN_KV_FP8_E4M3, s->mode, S, W_auto};
     }
     return ATTN_OK;
 }
@@ -197,7 +233,15 @@ int32_t attn_static_splits(const attn_shape *shape)
     Shape s;
     if (check(shape, &s) != ATTN_OK)
         return 0;
-    return effective_splits(shape);
+    return effective_splits(shape, s.W);
+}
+
+int32_t attn_num_wgs(const attn_shape *shape)
+{
+    Shape s;
+    if (check(shape, &s) != ATTN_OK)
+        return 0;
+    return s.W;
 }
 
 int attn_device_cu_count(int device, int32_t *cus)
@@ -266,6 +310,8 @@ static int enqueue_plan(const Shape &s, const WsLayout &L, const int32_t *length
     a.num_pages = s.num_pages;
     a.T = s.T;
     a.W = s.W;
+    a.W_auto = s.W_auto;
+    a.W_auto = s.W_auto;
     a.mode = s.mode;
     a.S = s.S;
     const hipError_t e = launch_plan(a, st);
@@ -464,6 +510,7 @@ static int enqueue_step(const Shape &s, const void *q, const void *k_cache, cons
     a.S = s.S;
     a.T = s.T;
     a.W = s.W;
+    a.W_auto = s.W_auto;
     a.slot_rows = slot_rows;
     a.scale_log2 = sm_scale * 1.4426950408889634f;
     const int grid = s.mode == ATTN_STATIC ? s.B * s.Hkv * s.S : s.W;

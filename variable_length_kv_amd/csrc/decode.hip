@@ -592,7 +592,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
             if (tid == 0)
                 lds.tp[0] = 0;
             N = (int64_t)total * a.Hkv;
-            We = N < a.W ? N : a.W;
+            We = plan_wgs(N, a.W, a.W_auto);
             __syncthreads();   // the tiles prefix and the lengths are complete
             // requests without tiles: o = 0, lse = -inf (spread over the grid)
             for (int bb = w; bb < a.B; bb += gridDim.x) {

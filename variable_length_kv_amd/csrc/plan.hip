@@ -11,7 +11,9 @@
 //   units   (b, g, t), t < ceil(Le_b / T), numbered b-major, then g, then t;
 //           Le_b = L_b if 0 <= L_b <= pt_stride*P, else 0 (status bit 1)
 //   dynamic workgroup w owns units [floor(w*N/We), floor((w+1)*N/We)),
-//           We = min(W, N); unit u's owner is floor(((u+1)*We - 1) / N);
+//           We = min(W, N) (W: the launch's count, or by default two per
+//           compute unit when that leaves 32 units each, else one);
+//           unit u's owner is floor(((u+1)*We - 1) / N);
 //           pair bg = b*Hkv+g has owner(last) - owner(first) + 1 segments,
 //           each with a partial slot seg_prefix[bg] + (w - first_wg[bg])
 //   static  chunk C = ceil(max Le / S) rounded up to lcm(P, T); split s of a
@@ -54,7 +56,7 @@ __device__ void plan_partition(const PlanArgs &a, const int32_t *tp, int n, int 
     // segments per (item, g) and their prefix
     const int nbg = n * a.Hkv;
     const int64_t N = (int64_t)total * a.Hkv;
-    const int64_t We = N < a.W ? N : a.W;
+    const int64_t We = plan_wgs(N, a.W, a.W_auto);
     const int cB = (nbg + NT - 1) / NT;
     const int g0 = min(nbg, tid * cB), g1 = min(nbg, g0 + cB);
     int segs = 0;

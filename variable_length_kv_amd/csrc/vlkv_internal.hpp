@@ -57,8 +57,19 @@ enum PlanSrc : int {
 
 __host__ __device__ constexpr bool is_shared(int src) { return src == SRC_SHARED || src == SRC_SHARED_WIDE; }
 
+// Workgroups a dynamic plan of N units uses. W is the launch's workgroup
+// count; with the library default (W_auto = the device's compute units,
+// W = 2 * W_auto) two per compute unit when that leaves at least 32 units per
+// workgroup, else one per compute unit. Never more than N.
+__host__ __device__ inline int64_t plan_wgs(int64_t N, int W, int W_auto)
+{
+    const int64_t Wu = (W_auto > 0 && N < 32 * (int64_t)W) ? W_auto : W;
+    return N < Wu ? N : Wu;
+}
+
 struct Shape {
     int B, Hq, Hkv, G, D, P, num_pages, pt_stride, T, W, kv_fp8, mode, S;
+    int W_auto;   // compute units when num_wgs = 0 chose W = 2 * W_auto, else 0
 };
 
 WsLayout ws_layout(const Shape &s);
@@ -70,6 +81,7 @@ struct PlanArgs {
     // mode 2 only
     int32_t *item_req, *item_start, *item_m, *item_solo, *req_shared, *req_member, *req_own;
     int B, Hkv, G, P, pt_stride, num_pages, T, W, mode, S;
+    int W_auto;   // see plan_wgs
 };
 
 struct DecodeArgs {
@@ -87,6 +99,7 @@ struct DecodeArgs {
     uint16_t *out;             // [B][Hq][D] bf16 bits
     float *lse;                // [B][Hq] or null
     int B, Hq, Hkv, G, P, num_pages, pt_stride, blocks_per_tile, S, T, W;
+    int W_auto;                // see plan_wgs (single launch, dynamic)
     int slot_rows;             // query rows per partial slot
     float scale_log2;          // sm_scale * log2(e)
 };

@@ -22,7 +22,7 @@ ATTN_KV_BF16, ATTN_KV_FP8_E4M3 = 0, 1
 ATTN_DYNAMIC, ATTN_STATIC, ATTN_SHARED = 0, 1, 2
 ATTN_STATUS_BAD_LENGTH, ATTN_STATUS_BAD_PAGE, ATTN_STATUS_INTERNAL = 1, 2, 4
 
-EXPORTED = ("attn_check_shape", "attn_workspace_bytes", "attn_static_splits", "attn_device_cu_count",
+EXPORTED = ("attn_check_shape", "attn_workspace_bytes", "attn_static_splits", "attn_num_wgs", "attn_device_cu_count",
             "attn_plan", "attn_decode", "attn_combine", "attn_get_status", "attn_read_plan",
             "attn_workspace_init", "attn_step", "attn_step_noalloc", "attn_append_kv", "attn_read_plan_items",
             "attn_last_error",
@@ -49,7 +49,7 @@ class AttnShape:
     page_size: int
     num_pages: int
     pt_stride: int
-    num_wgs: int
+    num_wgs: int = 0   # 0: the library default (see the C header)
     head_dim: int = 128
     tile_tokens: int = 64
     kv_dtype: int = ATTN_KV_BF16
@@ -79,6 +79,7 @@ def load():
         "attn_check_shape": (i32, [SP]),
         "attn_workspace_bytes": (sz, [SP]),
         "attn_static_splits": (i32, [SP]),
+        "attn_num_wgs": (i32, [SP]),
         "attn_device_cu_count": (i32, [ctypes.c_int, P]),
         "attn_plan": (i32, [SP, P, P, P, sz, P]),
         "attn_decode": (i32, [SP, P, P, P, P, P, P, ctypes.c_float, P, sz, P, P, P]),
@@ -217,15 +218,13 @@ def attn_static_splits(shape) -> int:
     return int(load().attn_static_splits(_shape(shape)))
 
 
-def suggest_num_wgs(cus: int, lengths, num_kv_heads: int, tile_tokens: int = 64, min_units: int = 32) -> int:
-    """Workgroup count for the dynamic plan: two per compute unit (two waves per
-    SIMD hide load latency best on large batches), or one per compute unit when
-    two would leave fewer than ``min_units`` tiles per workgroup, where the fixed
-    per-workgroup costs (plan prologue, segment merges) would dominate."""
-    import numpy as np
-    L = np.asarray(lengths, np.int64)
-    units = int(((np.maximum(L, 0) + tile_tokens - 1) // tile_tokens).sum()) * num_kv_heads
-    return 2 * cus if units >= 2 * cus * min_units else cus
+def attn_num_wgs(shape) -> int:
+    """Workgroups of the decode launch (resolves num_wgs = 0 on the current device)."""
+    n = int(load().attn_num_wgs(_shape(shape)))
+    if n == 0:
+        attn_check_shape(shape)
+        raise AttnError(ATTN_ERR_INVALID_ARG, load().attn_last_error().decode())
+    return n
 
 
 def attn_device_cu_count(device: int = 0) -> int:
@@ -300,7 +299,7 @@ def attn_read_plan(shape, workspace, stream=None) -> dict:
     """The plan arrays of the workspace. ATTN_SHARED: over items (cut to the
     header's item count), plus the item description."""
     import numpy as np
-    B, Hkv, W = shape.batch, shape.num_kv_heads, shape.num_wgs
+    B, Hkv, W = shape.batch, shape.num_kv_heads, attn_num_wgs(shape)
     n = 2 * B if shape.mode == ATTN_SHARED else B
     out = {
         "header": np.zeros(8, np.int32), "len_eff": np.zeros(n, np.int32),

@@ -216,6 +216,33 @@ def make_case(name, lengths, *, Hq=8, Hkv=1, P=16, D=HEAD_DIM, kv_dtype="bf16",
                 float(sm_scale), {"seed": seed})
 
 
+def sub_case(case: Case, ids) -> Case:
+    """The requests ``ids`` of a decode step as a batch of their own, with
+    only their pages (renumbered in order of first use) and their scales: a
+    compact host copy of part of a step, e.g. one of a trace whose caches
+    change afterwards. Pure input bookkeeping."""
+    ids = [int(i) for i in ids]
+    P = case.P
+    lengths = np.asarray(case.lengths, np.int64)[ids]
+    n = (np.maximum(lengths, 0) + P - 1) // P
+    stride = max(1, int(n.max()) if len(n) else 1)
+    pt = np.full((len(ids), stride), -1, np.int32)
+    pages, index = [], {}
+    for r, b in enumerate(ids):
+        for j in range(int(n[r])):
+            p = int(case.page_table[b, j])
+            if p not in index:
+                index[p] = len(pages)
+                pages.append(p)
+            pt[r, j] = index[p]
+    sel = torch.tensor(pages if pages else [0], dtype=torch.int64)
+    ks = case.k_scale[ids].clone() if case.k_scale is not None else None
+    vs = case.v_scale[ids].clone() if case.v_scale is not None else None
+    return Case(f"{case.name}[{len(ids)}]", len(ids), case.Hq, case.Hkv, case.D, P, lengths.astype(np.int32), pt,
+                max(1, len(pages)), case.kv_dtype, case.q[ids].clone(), case.k_cache[sel].clone(),
+                case.v_cache[sel].clone(), ks, vs, case.sm_scale, dict(case.meta, ids=ids))
+
+
 def shared_page_table(lengths, groups, P, seed):
     """Page table with prefix caching: ``groups`` lists (first, count,
     prefix_pages); requests first+1 .. first+count-1 read request first's
