@@ -381,7 +381,6 @@ static int enqueue_decode(const Shape &s, const WsLayout &L, const void *q, cons
     a.P = s.P;
     a.num_pages = s.num_pages;
     a.pt_stride = s.pt_stride;
-    a.blocks_per_tile = s.T / kBlockTokens;
     a.S = s.S;
     a.T = s.T;
     a.W = s.W;
@@ -506,7 +505,6 @@ static int enqueue_step(const Shape &s, const void *q, const void *k_cache, cons
     a.P = s.P;
     a.num_pages = s.num_pages;
     a.pt_stride = s.pt_stride;
-    a.blocks_per_tile = s.T / kBlockTokens;
     a.S = s.S;
     a.T = s.T;
     a.W = s.W;

@@ -112,6 +112,13 @@ __device__ __forceinline__ s16x4 pack_bf16x4(f32x4 x)
     return __builtin_bit_cast(s16x4, (u32x2){__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)});
 }
 
+// Two packed 4-value operands side by side: an 8-value MFMA operand.
+__device__ __forceinline__ bf16x8 cat_bf16x8(s16x4 a, s16x4 b)
+{
+    const u32x2 x = __builtin_bit_cast(u32x2, a), y = __builtin_bit_cast(u32x2, b);
+    return __builtin_bit_cast(bf16x8, (u32x4){x[0], x[1], y[0], y[1]});
+}
+
 // The bf16 values of a packed operand, widened back to fp32 (exact).
 __device__ __forceinline__ f32x4 unpack_bf16x4(s16x4 v)
 {
@@ -189,9 +196,12 @@ struct Meta {
 // Walks a workgroup's blocks in order. SRC_DYNAMIC / SRC_FUSED_DYNAMIC /
 // SRC_SHARED: the contiguous unit range of the plan (SRC_SHARED: over items,
 // b is then the item index); SRC_STATIC / SRC_FUSED_STATIC: the one
-// (b, g, split) of this workgroup.
-template <int SRC>
+// (b, g, split) of this workgroup. A block is KBT tokens counted from its
+// segment's first token (a segment starts at a tile boundary), one slice of
+// KBT / kWaves tokens per wave; a segment's last block may be short.
+template <int SRC, int KBT>
 struct Walker {
+    static constexpr int kSliceT = KBT / kWaves;   // tokens per wave per block
     static constexpr bool kFused = SRC == SRC_FUSED_DYNAMIC || SRC == SRC_FUSED_STATIC;
     static constexpr bool kShared = is_shared(SRC);
     static constexpr bool kPlanned = SRC == SRC_DYNAMIC || kShared;   // ranges from attn_plan's arrays
@@ -199,7 +209,8 @@ struct Walker {
 
     const DecodeArgs *a;
     int w, wave;
-    int b, g, blk, blk0, blk_end, L, nt, units_left, done;
+    int b, g, L, nt, units_left, done;
+    int tok, tok_seg, tok_end;   // current block's first token, the segment's first and end tokens
     int slot, direct, nseg, wfirst, first_off;
     // SRC_SHARED: the item's first request, first token, request count and
     // whether it is its request's only item
@@ -241,10 +252,8 @@ struct Walker {
 
     __device__ void enter_segment(int ta, int tb)
     {
-        const int R = a->blocks_per_tile;
-        blk = blk0 = ta * R;
-        const int nblk = (L + kBlockTokens - 1) / kBlockTokens;
-        blk_end = min(tb * R, nblk);
+        tok = tok_seg = ta * a->T;
+        tok_end = (int)min((int64_t)tb * a->T, (int64_t)L);
         const int bg = b * a->Hkv + g;
         if (kPlanned) {
             const int s0 = ldc(a->seg_prefix, bg);
@@ -333,13 +342,13 @@ struct Walker {
             slot = w;
             direct = S == 1;
             nseg = S;
-            blk = blk0 = lo / kBlockTokens;
+            tok = tok_seg = lo;
             if (hi > lo) {
-                blk_end = (hi + kBlockTokens - 1) / kBlockTokens;
+                tok_end = hi;
             } else {
                 // empty split: one pseudo-block without valid tokens, so the
                 // workgroup still writes its (empty) result
-                blk_end = blk + 1;
+                tok_end = lo + 1;
                 L = 0;
             }
         }
@@ -361,11 +370,11 @@ struct Walker {
     // segments; the walker itself is not advanced).
     __device__ int count_blocks() const
     {
+        const int n0 = tok < tok_end ? (tok_end - tok + KBT - 1) / KBT : 0;
         if (!kDyn)
-            return blk_end - blk;
-        int n = blk_end - blk;
+            return n0;
+        int n = n0;
         int bb = b, gg = g, ntt = nt, LL = L, left = units_left;
-        const int R = a->blocks_per_tile;
         while (left > 0) {
             if (++gg == a->Hkv) {
                 gg = 0;
@@ -377,7 +386,7 @@ struct Walker {
             }
             const int take = min(ntt, left);
             left -= take;
-            n += min(take * R, (LL + kBlockTokens - 1) / kBlockTokens);
+            n += (int)((min((int64_t)take * a->T, (int64_t)LL) + KBT - 1) / KBT);
         }
         return n;
     }
@@ -390,10 +399,10 @@ struct Walker {
         m.valid = !done;
         m.b = b;
         m.g = g;
-        m.tok0 = blk * kBlockTokens + wave * kSlice;
-        m.nv = done ? 0 : max(0, min(kSlice, L - m.tok0));
-        m.first = !done && blk == blk0;
-        m.last = !done && blk + 1 == blk_end;
+        m.tok0 = tok + wave * kSliceT;
+        m.nv = done ? 0 : max(0, min(kSliceT, min(tok_end, L) - m.tok0));
+        m.first = !done && tok == tok_seg;
+        m.last = !done && tok + KBT >= tok_end;
         m.slot = slot;
         m.direct = direct;
         m.nseg = nseg;
@@ -407,8 +416,8 @@ struct Walker {
         m.vsc = 1.f;
         if (done)
             return m;
-        ++blk;
-        if (blk == blk_end) {
+        tok += KBT;
+        if (tok >= tok_end) {
             if (kDyn && units_left > 0) {
                 ++g;
                 if (g == a->Hkv) {
@@ -553,6 +562,10 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
     constexpr int D = kHeadDim;
     constexpr int EB = KVFP8 ? 1 : 2;             // bytes per cached element
     constexpr int kSlots = 2;                      // slices in flight per wave
+    // block tokens: a wave's slice is 16 bf16 or 32 fp8 cache rows (4 KB of K
+    // and 4 KB of V either way)
+    constexpr int kBT = KVFP8 ? 128 : 64;
+    constexpr int kSliceT = kBT / kWaves;
     constexpr bool kEarlyRefill = NCB == 1;        // refill a slot before its block's math
     const size_t page_head_bytes = (size_t)a.P * D * EB;
 
@@ -634,7 +647,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
         sel8[s] = bits;
     }
 
-    Walker<SRC> wk;
+    Walker<SRC, kBT> wk;
     wk.init(&a, w, wave, lds.tp, lds.len, N, We, chunk);
 
     // per-wave softmax state, head = row. m_run is uniform over the 4 row
@@ -707,46 +720,81 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
         if (m.valid && m.first)
             load_q(s.q, m, 0, m.ksc, m.vsc);
     };
-    // page id of a block's slice (a scalar load), or -1 when it has no rows
-    auto slice_page = [&](const Meta &m) -> int {
+    // page ids of a block's slice (scalar loads), -1 when it has no rows. An
+    // fp8 slice (32 rows) starts on a 32-token boundary; its second half is on
+    // another page only when the page size is an odd multiple of 16.
+    struct Pages {
+        int p0, p1;   // pages of the slice's rows 0-15 and (fp8) 16-31
+        int r0;       // row of the slice's first token in page p0
+    };
+    auto slice_pages = [&](const Meta &m) -> Pages {
         if (!m.valid || m.nv <= 0)
-            return -1;
-        return ldc(a.page_table, (size_t)m.b * a.pt_stride + (m.tbase + m.tok0) / a.P);
+            return {-1, -1, 0};
+        const int tok = m.tbase + m.tok0;   // token index in the request
+        const int pi = tok / a.P, r0 = tok - pi * a.P;
+        const size_t base = (size_t)m.b * a.pt_stride;
+        const int p0 = ldc(a.page_table, base + pi);
+        int p1 = p0;
+        if (KVFP8 && m.nv > 16 && r0 + 16 >= a.P)
+            p1 = ldc(a.page_table, base + pi + 1);
+        return {p0, p1, r0};
     };
     // The slice's K and V rows are read through buffer descriptors whose base
     // is the slice's first row (wave-uniform, scalar registers) and whose
     // range is exactly its valid rows: a row past the request's length, or a
     // whole slice past the end of the work or on an invalid page (range 0),
     // reads as zeros without touching memory. Each lane adds its fixed 32-bit
-    // offset (16 bytes per lane, 1 KB per load).
-    auto load_slice = [&](Slot &s, Meta &m, int page) {
-        size_t slab = 0;
-        int nrec = 0;
+    // offset (16 bytes per lane, 1 KB per load): four loads of K and four of
+    // V, 16 bf16 rows or 32 fp8 rows (the second 16 through a second
+    // descriptor, their page being possibly another).
+    auto load_slice = [&](Slot &s, Meta &m, Pages pg) {
+        constexpr int RB = D * EB;   // bytes per cache row
+        size_t slab0 = 0, slab1 = 0;
+        int n0 = 0, n1 = 0;
         if (m.valid && m.nv > 0) {
-            if (page < 0 || page >= a.num_pages) {
+            const bool bad1 = KVFP8 && m.nv > 16 && (pg.p1 < 0 || pg.p1 >= a.num_pages);
+            if (pg.p0 < 0 || pg.p0 >= a.num_pages || bad1) {
                 bad_page = 1;   // reported once at the end of the kernel
                 m.nv = 0;
             } else {
-                const int tok = m.tbase + m.tok0;   // token index in the request
-                slab = ((size_t)page * a.Hkv + m.g) * page_head_bytes + (size_t)(tok % a.P) * (D * EB);
-                // (wave-uniform; kept in a scalar register so that the
-                // descriptor is, and the loads need no per-lane loop)
-                nrec = __builtin_amdgcn_readfirstlane(m.nv * (D * EB));
+                slab0 = ((size_t)pg.p0 * a.Hkv + m.g) * page_head_bytes + (size_t)pg.r0 * RB;
+                // (wave-uniform; kept in scalar registers so that the
+                // descriptors are, and the loads need no per-lane loop)
+                n0 = __builtin_amdgcn_readfirstlane(min(m.nv, 16) * RB);
+                if (KVFP8) {
+                    const int r1 = pg.r0 + 16 >= a.P ? pg.r0 + 16 - a.P : pg.r0 + 16;
+                    slab1 = ((size_t)pg.p1 * a.Hkv + m.g) * page_head_bytes + (size_t)r1 * RB;
+                    n1 = __builtin_amdgcn_readfirstlane(max(m.nv - 16, 0) * RB);
+                }
             }
         }
-        const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.k + slab), 0, nrec, kRsrcWord3);
-        const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.v + slab), 0, nrec, kRsrcWord3);
-        constexpr int NL = KVFP8 ? 2 : 4;
+        const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.k + slab0), 0, n0, kRsrcWord3);
+        const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.v + slab0), 0, n0, kRsrcWord3);
+        if (KVFP8) {
+            const auto rk1 = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.k + slab1), 0, n1, kRsrcWord3);
+            const auto rv1 = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.v + slab1), 0, n1, kRsrcWord3);
 #pragma unroll
-        for (int i = 0; i < NL; ++i)
-            s.k[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, 16 * lane + 1024 * i, 0, kLoadNT));
+            for (int i = 0; i < 2; ++i) {
+                s.k[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, 16 * lane + 1024 * i, 0, kLoadNT));
+                s.k[2 + i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk1, 16 * lane + 1024 * i, 0, kLoadNT));
+            }
 #pragma unroll
-        for (int i = 0; i < NL; ++i)
-            s.v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, 16 * lane + 1024 * i, 0, kLoadNT));
+            for (int i = 0; i < 2; ++i) {
+                s.v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, 16 * lane + 1024 * i, 0, kLoadNT));
+                s.v[2 + i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv1, 16 * lane + 1024 * i, 0, kLoadNT));
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                s.k[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, 16 * lane + 1024 * i, 0, kLoadNT));
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                s.v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, 16 * lane + 1024 * i, 0, kLoadNT));
+        }
     };
     auto issue = [&](Slot &s, Meta &m) {
         next_block(s, m);
-        load_slice(s, m, slice_page(m));
+        load_slice(s, m, slice_pages(m));
     };
 
     // ---- end of a segment: merge the 4 waves and write ------------------
@@ -851,17 +899,18 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
     auto compute = [&](Slot &s, Meta &mslot) {
         const Meta mcopy = mslot;   // the slot's description is replaced by the refill
         const Meta &mt = kEarlyRefill ? mcopy : mslot;
-        constexpr int NL = KVFP8 ? 2 : 4;
+        constexpr int NL = 4;
         // operand registers: the slot's own once it is not refilled before the math
         u32x4 kbuf[4], vbuf[4];
         u32x4(&kop)[4] = kEarlyRefill ? kbuf : s.k;
         u32x4(&vop)[4] = kEarlyRefill ? vbuf : s.v;
-        // Load i of lane l brought slice bytes [1024 i + 16 l, +16): row
-        // (1024 i + 16 l) / RB, column byte (1024 i + 16 l) % RB, RB = D * EB.
-        // Write them to this wave's staging rows, then read back the operand
-        // layout (row = lane % 16, bytes 64 i + 16 * (lane / 16)). LDS
-        // operations of one wave complete in order, so no barrier is needed.
-        constexpr int RB = D * EB;
+        // Load i of lane l brought slice bytes [1024 i + 16 l, +16): staged row
+        // (1024 i + 16 l) / 256, column byte (1024 i + 16 l) % 256 (a staged row
+        // is one bf16 cache row, or two fp8 cache rows). Write them to this
+        // wave's staging rows, then read back the operand layout (row = lane %
+        // 16, bytes 64 i + 16 * (lane / 16)). LDS operations of one wave
+        // complete in order, so no barrier is needed.
+        constexpr int RB = 256;
         uint8_t *sk = lds.stg[wave][0];
         uint8_t *sv = lds.stg[wave][1];
 #pragma unroll
@@ -908,52 +957,63 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
             vop[i] = *reinterpret_cast<const u32x4 *>(sv + o);
         }
         {
-            // scores: S^T[token 4*grp+i][head row], per column block
-            f32x4 st[NCB];
+            // Scores S^T[sub-tile row 4*grp+i][head row], per column block and
+            // 16-token sub-tile: sub-tile s, row m is token m (bf16) or 2m + s
+            // (fp8: a staged row holds two cache rows), so each fp8 sub-tile
+            // reads its own half of the staged row pairs.
+            constexpr int NST = KVFP8 ? 2 : 1;   // 16-token sub-tiles per slice
+            f32x4 st[NCB][NST];
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb)
-                st[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (KVFP8) {
+#pragma unroll
+                for (int sub = 0; sub < NST; ++sub)
+                    st[cb][sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int sub = 0; sub < NST; ++sub) {
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
-                    const uint32_t w0 = kop[kk >> 1][2 * (kk & 1)];
-                    const uint32_t w1 = kop[kk >> 1][2 * (kk & 1) + 1];
-                    const bf16x2 c0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
-                    const bf16x2 c1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
-                    const bf16x2 c2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
-                    const bf16x2 c3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
-                    const bf16x8 kv = {c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
+                    bf16x8 kv;
+                    if (KVFP8) {
+                        const uint32_t w0 = kop[2 * sub + (kk >> 1)][2 * (kk & 1)];
+                        const uint32_t w1 = kop[2 * sub + (kk >> 1)][2 * (kk & 1) + 1];
+                        const bf16x2 c0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+                        const bf16x2 c1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+                        const bf16x2 c2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+                        const bf16x2 c3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+                        kv = bf16x8{c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
+                    } else {
+                        kv = __builtin_bit_cast(bf16x8, kop[kk]);
+                    }
 #pragma unroll
                     for (int cb = 0; cb < NCB; ++cb)
                         if (cb == 0 || two)
-                            st[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, __builtin_bit_cast(bf16x8, qreg[cb][kk]),
-                                                                             st[cb], 0, 0, 0);
+                            st[cb][sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                kv, __builtin_bit_cast(bf16x8, qreg[cb][kk]), st[cb][sub], 0, 0, 0);
                 }
-            } else {
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb)
-                    if (cb == 0 || two) {
-#pragma unroll
-                        for (int kk = 0; kk < 4; ++kk)
-                            st[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop[kk]),
-                                                                             __builtin_bit_cast(bf16x8, qreg[cb][kk]),
-                                                                             st[cb], 0, 0, 0);
-                    }
             }
-            s16x4 pb[NCB];
+            s16x4 pb[NCB][NST];
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
                 if (!(cb == 0 || two))
                     continue;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    st[cb][i] *= sc[cb];
-                if (mt.nv < kSlice) {
+                for (int sub = 0; sub < NST; ++sub)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        st[cb][i] = 4 * grp + i >= mt.nv ? -INFINITY : st[cb][i];
+                        st[cb][sub][i] *= sc[cb];
+                if (mt.nv < kSliceT) {
+#pragma unroll
+                    for (int sub = 0; sub < NST; ++sub)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int t = KVFP8 ? 2 * (4 * grp + i) + sub : 4 * grp + i;
+                            st[cb][sub][i] = t >= mt.nv ? -INFINITY : st[cb][sub][i];
+                        }
                 }
-                float mx = fmaxf(fmaxf(st[cb][0], st[cb][1]), fmaxf(st[cb][2], st[cb][3]));
+                float mx = -INFINITY;
+#pragma unroll
+                for (int sub = 0; sub < NST; ++sub)
+                    mx = fmaxf(mx, fmaxf(fmaxf(st[cb][sub][0], st[cb][sub][1]), fmaxf(st[cb][sub][2], st[cb][sub][3])));
                 mx = xmax4(mx);
                 // Lazy rescaling: the reference maximum m_run only moves (and the
                 // running sums are rescaled) when a head's scores exceed it by more
@@ -972,14 +1032,17 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
                     m_run[cb] = m_new;
                 }
                 const float m_use = m_run[cb] == -INFINITY ? 0.f : m_run[cb];
-                f32x4 p;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    p[i] = fast_exp2(st[cb][i] - m_use);
-                pb[cb] = pack_bf16x4(p);
-                const f32x4 pr = unpack_bf16x4(pb[cb]);
-                l_run[cb] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-                e_run[cb] += (p[0] + p[1]) + (p[2] + p[3]);
+                for (int sub = 0; sub < NST; ++sub) {
+                    f32x4 p;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        p[i] = fast_exp2(st[cb][sub][i] - m_use);
+                    pb[cb][sub] = pack_bf16x4(p);
+                    const f32x4 pr = unpack_bf16x4(pb[cb][sub]);
+                    l_run[cb] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+                    e_run[cb] += (p[0] + p[1]) + (p[2] + p[3]);
+                }
             }
             // rows past the length were read as zeros (the loads' range ends at
             // the last valid row), so they add nothing to P.V
@@ -988,21 +1051,35 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
             for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
                 for (int ss = 0; ss < 2; ++ss) {
-                    f32x4 t;
                     if (KVFP8) {
-                        const u32x2 src = {vop[kk >> 1][2 * (kk & 1)], vop[kk >> 1][2 * (kk & 1) + 1]};
-                        t = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(__builtin_bit_cast(long, src),
-                                                                       (long)sel8[ss], zero, 0, 0, 0);
-                    } else {
-                        t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vop[kk]),
-                                                                    sel16[ss], zero, 0, 0, 0);
-                    }
-                    const s16x4 vt = pack_bf16x4(t);
+                        // V^T of both sub-tiles side by side is the A operand of a
+                        // 32-deep product: lane l holds reduction index 8*grp + j,
+                        // the token of sub-tile j / 4, row 4*grp + j % 4; the two
+                        // sub-tiles' P^T side by side is the B operand in that order
+                        s16x4 vt[2];
 #pragma unroll
-                    for (int cb = 0; cb < NCB; ++cb)
-                        if (cb == 0 || two)
-                            acc[cb][2 * kk + ss] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pb[cb],
-                                                                                             acc[cb][2 * kk + ss], 0, 0, 0);
+                        for (int sub = 0; sub < 2; ++sub) {
+                            const u32x2 src = {vop[2 * sub + (kk >> 1)][2 * (kk & 1)],
+                                               vop[2 * sub + (kk >> 1)][2 * (kk & 1) + 1]};
+                            vt[sub] = pack_bf16x4(__builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
+                                __builtin_bit_cast(long, src), (long)sel8[ss], zero, 0, 0, 0));
+                        }
+                        const bf16x8 va = cat_bf16x8(vt[0], vt[1]);
+#pragma unroll
+                        for (int cb = 0; cb < NCB; ++cb)
+                            if (cb == 0 || two)
+                                acc[cb][2 * kk + ss] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    va, cat_bf16x8(pb[cb][0], pb[cb][NST - 1]), acc[cb][2 * kk + ss], 0, 0, 0);
+                    } else {
+                        const f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vop[kk]),
+                                                                                sel16[ss], zero, 0, 0, 0);
+                        const s16x4 vt = pack_bf16x4(t);
+#pragma unroll
+                        for (int cb = 0; cb < NCB; ++cb)
+                            if (cb == 0 || two)
+                                acc[cb][2 * kk + ss] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                                    vt, pb[cb][0], acc[cb][2 * kk + ss], 0, 0, 0);
+                    }
                 }
             }
         }
@@ -1021,13 +1098,13 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
     Meta mt[kSlots];
     {
         // the first blocks' page ids are fetched together (one round trip)
-        int pg[kSlots];
+        Pages pg[kSlots];
 #pragma unroll
         for (int i = 0; i < kSlots; ++i)
             next_block(sl[i], mt[i]);
 #pragma unroll
         for (int i = 0; i < kSlots; ++i)
-            pg[i] = slice_page(mt[i]);
+            pg[i] = slice_pages(mt[i]);
 #pragma unroll
         for (int i = 0; i < kSlots; ++i)
             load_slice(sl[i], mt[i], pg[i]);

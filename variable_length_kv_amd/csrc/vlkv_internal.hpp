@@ -10,8 +10,7 @@ namespace vlkv {
 
 constexpr int kHeadDim = 128;      // D supported by the decode kernel
 constexpr int kWaves = 4;          // wavefronts per decode workgroup
-constexpr int kSlice = 16;         // tokens per wave per 64-token block
-constexpr int kBlockTokens = 64;   // kWaves * kSlice
+constexpr int kBlockTokens = 64;   // tile granularity: 4 waves x 16 bf16 rows
 constexpr int kDecodeThreads = 256;
 constexpr int kMaxGroup = 16;      // query heads per kv head (one MFMA column block)
 constexpr int kMaxBatch = 8192;    // planner keeps the tile prefix in LDS
@@ -98,7 +97,7 @@ struct DecodeArgs {
     float *part_o, *part_lse;
     uint16_t *out;             // [B][Hq][D] bf16 bits
     float *lse;                // [B][Hq] or null
-    int B, Hq, Hkv, G, P, num_pages, pt_stride, blocks_per_tile, S, T, W;
+    int B, Hq, Hkv, G, P, num_pages, pt_stride, S, T, W;
     int W_auto;                // see plan_wgs (single launch, dynamic)
     int slot_rows;             // query rows per partial slot
     float scale_log2;          // sm_scale * log2(e)
