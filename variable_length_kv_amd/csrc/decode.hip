@@ -64,6 +64,7 @@ constexpr int kLdsRow = kHeadDim + 4;  // padded fp32 row of the merge buffer
 constexpr int kStgRow = kHeadDim * 2 + 16;  // padded byte row of a staged K or V slice
 constexpr float kLazy = 8.f;           // lazy-rescale threshold (log2 units)
 constexpr int kMergeBatch = 4;         // partials folded together by the LSE merge
+constexpr int kMailboxSpin = 1 << 22;  // bound of a mailbox wait (s_sleep 1 each, ~0.1 s)
 // Word 3 of a raw buffer descriptor (gfx9 family): 32-bit data format, no
 // swizzle, no index. A data format of 0 would make every access read zero.
 constexpr int kRsrcWord3 = 0x00020000;
@@ -80,7 +81,9 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // workgroup that is behind issues first whenever both are ready.
 __device__ __forceinline__ void set_progress_priority(int done, int total)
 {
-    const int64_t d = done, t = total;   // compares only: no division in the loop
+    // wave-uniform 32-bit compares (block counts stay far below 2^26): scalar
+    // instructions only, no division in the loop
+    const int d = __builtin_amdgcn_readfirstlane(done), t = __builtin_amdgcn_readfirstlane(total);
     if (2 * d < t)
         __builtin_amdgcn_s_setprio(3);
     else if (5 * d < 4 * t)
@@ -309,14 +312,18 @@ struct Walker {
                 u0 = (int)u_beg;
                 u1 = (int)u_end;
                 // largest b in [0, B) with Hkv * tp[b] <= u0: the request of unit u0
-                int lo = 0, hi = a->B - 1;
-                while (lo < hi) {
-                    const int mid = (lo + hi + 1) >> 1;
-                    const int t = __builtin_amdgcn_readfirstlane(lds_tp[mid]);
-                    if ((int64_t)t * a->Hkv <= u0)
-                        lo = mid;
-                    else
-                        hi = mid - 1;
+                // (tp is non-decreasing and tp[0] = 0). Each round, the wave's
+                // lanes test 64 evenly spaced candidates of the remaining range
+                // at once; the count of passing ones locates the answer within
+                // one stride (one round for B <= 64, two for B <= 4096).
+                int lo = 0, n = a->B;
+                const int lane = threadIdx.x & 63;
+                while (n > 1) {
+                    const int st = (n + 63) >> 6;
+                    const bool ok = lane * st < n && (int64_t)lds_tp[lo + lane * st] * a->Hkv <= u0;
+                    const int c = __builtin_popcountll(__builtin_amdgcn_ballot_w64(ok));   // >= 1 (lane 0)
+                    lo += (c - 1) * st;
+                    n = min(st, n - (c - 1) * st);
                 }
                 b = lo;
                 tpb = __builtin_amdgcn_readfirstlane(lds_tp[b]);
@@ -519,20 +526,107 @@ __device__ __forceinline__ void merge_partials(const float *part_o, const float 
     }
 }
 
+// The single launch's end-of-kernel merge of the (up to two) pairs this
+// workgroup arrived at last. Every partial of an item (up to kEndPre per pair)
+// is loaded before any is folded, for both pairs at once, so the merge costs
+// one memory round trip; the folds then run in the same batches and order as
+// merge_partials, so the results are bitwise those of the combine kernel.
+// base_of(k, s): partial row of head 0 of the s-th partial of pair k.
+constexpr int kEndPre = 8;
+template <typename BaseOf>
+__device__ __forceinline__ void merge_pairs_at_end(const float *part_o, const float *part_lse, int npairs,
+                                                   const int (&n)[2], const int (&b)[2], const int (&g)[2],
+                                                   BaseOf base_of, int G, int Hq, uint16_t *out, float *lse)
+{
+    constexpr int D = kHeadDim;
+    for (int idx = threadIdx.x; idx < G * 32; idx += kDecodeThreads) {
+        const int h = idx >> 5, d4 = (idx & 31) * 4;
+        float ls[2][kEndPre];
+        f32x4 xs[2][kEndPre];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+#pragma unroll
+            for (int j = 0; j < kEndPre; ++j) {
+                if (k < npairs && j < n[k]) {
+                    const size_t sl = (size_t)base_of(k, j) + h;
+                    ls[k][j] = part_lse[sl];
+                    xs[k][j] = *reinterpret_cast<const f32x4 *>(part_o + sl * D + d4);
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            if (k >= npairs)
+                continue;
+            float M = -INFINITY, den = 0.f;
+            f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s0 = 0; s0 < kEndPre; s0 += kMergeBatch) {
+                if (s0 >= n[k])
+                    break;
+                float lb[kMergeBatch];
+                f32x4 xb[kMergeBatch];
+#pragma unroll
+                for (int j = 0; j < kMergeBatch; ++j) {
+                    lb[j] = ls[k][s0 + j];
+                    xb[j] = xs[k][s0 + j];
+                }
+                merge_fold(M, den, o, lb, xb, n[k] - s0);
+            }
+            for (int s0 = kEndPre; s0 < n[k]; s0 += kMergeBatch) {   // pairs of more pieces
+                float lb[kMergeBatch];
+                f32x4 xb[kMergeBatch];
+#pragma unroll
+                for (int j = 0; j < kMergeBatch; ++j) {
+                    const size_t sl = (size_t)base_of(k, s0 + j < n[k] ? s0 + j : s0) + h;
+                    lb[j] = part_lse[sl];
+                    xb[j] = *reinterpret_cast<const f32x4 *>(part_o + sl * D + d4);
+                }
+                merge_fold(M, den, o, lb, xb, n[k] - s0);
+            }
+            merge_write(M, den, o, out, lse, (size_t)b[k] * Hq + (size_t)g[k] * G + h, d4);
+        }
+    }
+}
+
+// LDS of a decode workgroup. With one column block, the per-wave states of a
+// segment's end go to a mailbox of their own beside the staging rows, so a
+// wave posts its state without waiting for the others to finish staging; with
+// two column blocks (32 query rows) the mailbox would not fit beside the
+// staging rows at two workgroups per CU, so it aliases them.
+template <int NCB>
+struct DecodeLdsRegion {   // NCB == 1
+    uint8_t stg[kWaves][2][16 * kStgRow];          // per-wave K and V slice staging (during blocks)
+    float acc[kWaves][kMaxGroup * NCB][kLdsRow];   // per-wave states at a segment's end
+};
+template <>
+struct DecodeLdsRegion<2> {
+    union {
+        uint8_t stg[kWaves][2][16 * kStgRow];
+        float acc[kWaves][kMaxGroup * 2][kLdsRow];
+    };
+};
+
 template <int NCB>
 struct DecodeLds {
     union {
-        float acc[kWaves][kMaxGroup * NCB][kLdsRow];  // per-wave states at a segment's end
-        uint8_t stg[kWaves][2][16 * kStgRow];          // per-wave K and V slice staging (during blocks)
+        DecodeLdsRegion<NCB> r;
         struct {
             int32_t tp[kMaxBatch + 1];          // single launch: tiles prefix (prologue only)
             int32_t len[kMaxBatch];             // and validated lengths
         };
     };
-    float m[kWaves][kMaxGroup * NCB];
-    float l[kWaves][kMaxGroup * NCB];
-    float e[kWaves][kMaxGroup * NCB];
+    // per mailbox buffer (two only with one column block and G <= 8)
+    float m[2][kWaves][kMaxGroup * NCB];
+    float l[2][kWaves][kMaxGroup * NCB];
+    float e[2][kWaves][kMaxGroup * NCB];
     int red[3 * kWaves];
+    // one column block: the latest segment end reached by any wave, and per
+    // buffer, counted from the block loop's start, the states posted (kWaves
+    // per segment) and the segments merged; the held segments' descriptions
+    int mb_first, mb_posted[2], mb_merged[2];
+    int mb_desc[2][8];   // b, g, slot, direct, nseg, wfirst, first_off, m
+    float mb_vsc[2];
     // single launch: the split pairs this workgroup arrived at last, merged
     // after its block loop (at most two: only a first and a last segment split)
     int npend;
@@ -673,8 +767,11 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
     }
 
     int bad_page = 0;
-    if (kFused && threadIdx.x == 0)
-        lds.npend = 0;   // read after the barriers of the first segment end
+    if (threadIdx.x == 0) {
+        lds.npend = 0;   // these are read after the barrier before the block loop
+        lds.mb_first = -1;
+        lds.mb_posted[0] = lds.mb_posted[1] = lds.mb_merged[0] = lds.mb_merged[1] = 0;
+    }
 
     // ---- loads of one block into a slot ---------------------------------
     // K/V loads are issued for every slot, also past the end of the work or
@@ -798,55 +895,83 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
     };
 
     // ---- end of a segment: merge the 4 waves and write ------------------
-    auto finish = [&](const Meta &mt) {
-        const int rows = mt.m * G;   // query rows of this segment
-        __syncthreads();   // every wave is done with its staging rows, which alias lds.acc
+    // The mailbox: per wave, the segment's running max and sums per query row
+    // and its o rows. One column block with G <= 8 (and not a shared prefix,
+    // whose items stack up to 16 rows): two buffers of 8 rows in the same
+    // LDS, used by alternate segments; otherwise one buffer.
+    const int nbuf = NCB == 1 && !is_shared(SRC) && G <= kMaxGroup / 2 ? 2 : 1;
+    const int rows_buf = kMaxGroup * NCB / nbuf;
+    auto acc_row = [&](int buf, int v, int r) -> float * {
+        return &lds.r.acc[0][0][0] + ((buf * kWaves + v) * rows_buf + r) * kLdsRow;
+    };
+    // Post this wave's state of the segment (running max, sums and o) to a buffer.
+    auto post_state = [&](int rows, int buf) {
+        // (the lane's LDS addresses are recomputed here from an opaque copy of
+        // the thread index rather than kept in registers across the block loop)
+        int t = threadIdx.x;
+        asm volatile("" : "+v"(t));
+        const int prow = t & 15, pgrp = (t & 63) >> 4;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
             const float l_tot = xsum4(l_run[cb]);
             const float e_tot = xsum4(e_run[cb]);
-            const int rr = 16 * cb + row;
+            const int rr = 16 * cb + prow;
             if (rr < rows) {
-                if (grp == 0) {
-                    lds.m[wave][rr] = m_run[cb];
-                    lds.l[wave][rr] = l_tot;
-                    lds.e[wave][rr] = e_tot;
+                if (pgrp == 0) {
+                    lds.m[buf][wave][rr] = m_run[cb];
+                    lds.l[buf][wave][rr] = l_tot;
+                    lds.e[buf][wave][rr] = e_tot;
                     if (is_shared(SRC) && wave == 0)
                         lds.vs[rr] = vsc_run[cb];   // per row: its request's V scale
                 }
+                float *ar = acc_row(buf, wave, rr);
 #pragma unroll
                 for (int mb = 0; mb < 8; ++mb) {
                     if (KVFP8) {
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
-                            lds.acc[wave][rr][out_dim<1>(mb, 4 * grp + i)] = acc[cb][mb][i];
+                            ar[out_dim<1>(mb, 4 * pgrp + i)] = acc[cb][mb][i];
                     } else {
-                        *reinterpret_cast<f32x4 *>(&lds.acc[wave][rr][16 * mb + 4 * grp]) = acc[cb][mb];
+                        *reinterpret_cast<f32x4 *>(ar + 16 * mb + 4 * pgrp) = acc[cb][mb];
                     }
                 }
             }
         }
-        __syncthreads();
-        const int tid = threadIdx.x;
-        for (int idx = tid; idx < rows * 32; idx += kDecodeThreads) {
+    };
+    // Merge the four states of a buffer and write the segment's output (a
+    // direct result or a partial), items t0, t0 + step, ...; thread t0 == 0
+    // also records a split pair for the end of the launch.
+    auto merge_out = [&](const Meta &mt, int rows, float vsc, int buf, int t0, int step) {
+        asm volatile("" : "+v"(t0));   // (addresses from t0 are not hoisted into the block loop)
+#pragma unroll 1
+        for (int idx = t0; idx < rows * 32; idx += step) {
             const int h = idx >> 5, d4 = (idx & 31) * 4;
+            // every wave's state is read before any is used (one LDS round trip)
+            float mv[kWaves], lv[kWaves], ev[kWaves];
+            f32x4 xv[kWaves];
+#pragma unroll
+            for (int v = 0; v < kWaves; ++v) {
+                mv[v] = lds.m[buf][v][h];
+                lv[v] = lds.l[buf][v][h];
+                ev[v] = lds.e[buf][v][h];
+                xv[v] = *reinterpret_cast<const f32x4 *>(acc_row(buf, v, h) + d4);
+            }
             float M = -INFINITY;
 #pragma unroll
             for (int v = 0; v < kWaves; ++v)
-                M = fmaxf(M, lds.m[v][h]);
+                M = fmaxf(M, mv[v]);
             f32x4 o = {0.f, 0.f, 0.f, 0.f};
             float lse2 = -INFINITY;
             if (M != -INFINITY) {
                 float den = 0.f, ex = 0.f;
 #pragma unroll
                 for (int v = 0; v < kWaves; ++v) {
-                    const float e = fast_exp2(lds.m[v][h] - M);
-                    den += e * lds.l[v][h];
-                    ex += e * lds.e[v][h];
-                    const f32x4 x = *reinterpret_cast<const f32x4 *>(&lds.acc[v][h][d4]);
-                    o += e * x;
+                    const float e = fast_exp2(mv[v] - M);
+                    den += e * lv[v];
+                    ex += e * ev[v];
+                    o += e * xv[v];
                 }
-                const float r = (is_shared(SRC) ? lds.vs[h] : vsc_run[0]) / den;
+                const float r = (is_shared(SRC) ? lds.vs[h] : vsc) / den;
                 o *= r;
                 lse2 = M + log2f(ex);
             }
@@ -871,26 +996,112 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
                     a.part_lse[prow] = lse2;
             }
         }
-        if (kFused && !mt.direct && tid == 0) {
+        if (kFused && !mt.direct && t0 == 0) {
             // The pair's arrival is deferred to the end of this workgroup's
             // blocks (no wait for the stores here, so the loads in flight keep
             // streaming). A contiguous unit range splits at most its first and
             // last pair; a third would break the plan's invariant and is
-            // reported instead of merged.
-            const int k = lds.npend;
+            // reported instead of merged. (Two merges may run at once, in two
+            // waves: the list's slot is taken atomically.)
+            const int k = __hip_atomic_fetch_add(&lds.npend, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             if (k < 2) {
                 lds.pend[k][0] = mt.b;
                 lds.pend[k][1] = mt.g;
                 lds.pend[k][2] = mt.nseg;
                 lds.pend[k][3] = mt.wfirst;
                 lds.pend[k][4] = mt.first_off;
-                lds.npend = k + 1;
             } else {
                 atomicOr(reinterpret_cast<unsigned *>(a.header + H_STATUS), kStatusInternal);
             }
         }
-        __syncthreads();
     };
+    // One column block: a segment's end does not stop the waves. Each wave
+    // posts its state to the segment's mailbox buffer and goes on with its
+    // next block. The first wave to reach the next segment's end (the wave
+    // with the most slack) merges the segment as soon as all four have posted
+    // it, which frees its buffer; the last segment is merged by every thread
+    // after the block loop. A wave waits only to post into a buffer whose
+    // previous segment is not merged yet. The first wave at segment end j is
+    // the one whose atomic max of j into mb_first returns less than j (the
+    // waves may reach different segment ends in any interleaving; mb_first
+    // only grows). Ordering: each post ends with a release increment of its
+    // buffer's mb_posted (workgroup scope, LDS), which the merging wave
+    // acquires before reading; the merge ends with a release of the buffer's
+    // mb_merged, which a wave acquires before writing the buffer again. Waits
+    // cannot last (every wave reaches each segment end after finitely many
+    // blocks, and each merge waits only for posts that wait only for earlier
+    // merges); they are still bounded, and a wait that ran out is reported in
+    // the status word (its merge is then skipped).
+    // Two column blocks: the mailbox aliases the staging rows, so all waves
+    // meet at barriers: post, merge (one item per thread), and go on.
+    int seg_idx = 0;   // segment ends this wave has passed (the same in every wave)
+    auto wait_at_least = [&](int *ctr, int v) -> bool {
+        for (int spin = 0; __hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < v; ++spin) {
+            if (spin >= kMailboxSpin) {
+                if (lane == 0)
+                    atomicOr(reinterpret_cast<unsigned *>(a.header + H_STATUS), kStatusInternal);
+                return false;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        return true;
+    };
+    // merge the segment held in a buffer (items t0, t0 + step, ...)
+    auto merge_held = [&](int buf, int t0, int step) {
+        Meta hm;
+        hm.b = __builtin_amdgcn_readfirstlane(lds.mb_desc[buf][0]);
+        hm.g = __builtin_amdgcn_readfirstlane(lds.mb_desc[buf][1]);
+        hm.slot = __builtin_amdgcn_readfirstlane(lds.mb_desc[buf][2]);
+        hm.direct = __builtin_amdgcn_readfirstlane(lds.mb_desc[buf][3]);
+        hm.nseg = __builtin_amdgcn_readfirstlane(lds.mb_desc[buf][4]);
+        hm.wfirst = __builtin_amdgcn_readfirstlane(lds.mb_desc[buf][5]);
+        hm.first_off = __builtin_amdgcn_readfirstlane(lds.mb_desc[buf][6]);
+        hm.m = __builtin_amdgcn_readfirstlane(lds.mb_desc[buf][7]);
+        merge_out(hm, hm.m * G, lds.mb_vsc[buf], buf, t0, step);
+    };
+    auto finish = [&](const Meta &mt) {
+        const int rows = mt.m * G;   // query rows of this segment
+        if (NCB == 1) {
+            const int j = seg_idx++;
+            const int buf = j & (nbuf - 1), use = nbuf == 2 ? j >> 1 : j;   // this segment's buffer and its use
+            int old = 0;
+            if (lane == 0)
+                old = __hip_atomic_fetch_max(&lds.mb_first, j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            old = __builtin_amdgcn_readfirstlane(old);
+            if (j > 0 && old < j) {
+                // first at this segment end: merge segment j - 1 once all four posted it
+                const int bp = (j - 1) & (nbuf - 1), up = nbuf == 2 ? (j - 1) >> 1 : j - 1;
+                if (wait_at_least(&lds.mb_posted[bp], kWaves * (up + 1)))
+                    merge_held(bp, lane, 64);
+                if (lane == 0)
+                    __hip_atomic_store(&lds.mb_merged[bp], up + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+            wait_at_least(&lds.mb_merged[buf], use);   // the buffer's previous segment is merged
+            post_state(rows, buf);
+            if (lane == 0) {
+                lds.mb_desc[buf][0] = mt.b;
+                lds.mb_desc[buf][1] = mt.g;
+                lds.mb_desc[buf][2] = mt.slot;
+                lds.mb_desc[buf][3] = mt.direct;
+                lds.mb_desc[buf][4] = mt.nseg;
+                lds.mb_desc[buf][5] = mt.wfirst;
+                lds.mb_desc[buf][6] = mt.first_off;
+                lds.mb_desc[buf][7] = mt.m;
+                lds.mb_vsc[buf] = vsc_run[0];
+                __hip_atomic_fetch_add(&lds.mb_posted[buf], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+        } else {
+            __syncthreads();   // every wave is done with its staging rows, which the mailbox aliases
+            post_state(rows, 0);
+            __syncthreads();
+            merge_out(mt, rows, vsc_run[0], 0, threadIdx.x, kDecodeThreads);
+            __syncthreads();
+        }
+    };
+
+    // a segment whose end is still to be posted (one column block)
+    Meta fin_mt;
+    bool pend_fin = false;
 
     // ---- math of one block ----------------------------------------------
     // The slot's K/V registers are staged into LDS first; the slot is then
@@ -911,8 +1122,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
         // 16, bytes 64 i + 16 * (lane / 16)). LDS operations of one wave
         // complete in order, so no barrier is needed.
         constexpr int RB = 256;
-        uint8_t *sk = lds.stg[wave][0];
-        uint8_t *sv = lds.stg[wave][1];
+        uint8_t *sk = lds.r.stg[wave][0];
+        uint8_t *sv = lds.r.stg[wave][1];
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             const int byte = 1024 * i + 16 * lane;
@@ -923,9 +1134,10 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
         // the second column block only when the segment's rows reach it
         // (wave-uniform: a shared item of more than 16 query rows)
         const bool two = NCB == 2 && mt.m * G > 16;
+        float ksc1 = 1.f, vsc1 = 1.f;
         if (mt.first) {
-            // q arrived with this slot (only a segment's first block loads it)
-            float ksc1 = 1.f, vsc1 = 1.f;
+            // q arrived with this slot (only a segment's first block loads it);
+            // copied before the refill reuses the slot's registers
             if (NCB == 2 && two)   // loaded here, once per segment (a memory round trip)
                 load_q(qreg[NCB - 1], mt, 1, ksc1, vsc1);
 #pragma unroll
@@ -935,6 +1147,22 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
                     const u32x4 q = cb == 0 ? s.q[kk] : qreg[cb][kk];
                     qreg[cb][kk] = (cb == 0 || two) && 16 * cb + row < mt.m * G ? q : u32x4{0u, 0u, 0u, 0u};
                 }
+            }
+        }
+        // (the two-column-block kernel refills after its math: its second
+        // block's state leaves no registers for a slice in flight beside the
+        // operands)
+        if (kEarlyRefill)
+            issue(s, mslot);
+        if (mt.first) {
+            // the previous segment's end, deferred to here so that both slots'
+            // loads are in flight while it runs
+            if (kEarlyRefill && pend_fin) {
+                finish(fin_mt);
+                pend_fin = false;
+            }
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
                 m_run[cb] = -INFINITY;
                 l_run[cb] = 0.f;
                 e_run[cb] = 0.f;
@@ -945,11 +1173,6 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
                 vsc_run[cb] = cb == 0 ? mt.vsc : vsc1;
             }
         }
-        // (the two-column-block kernel refills after its math: its second
-        // block's state leaves no registers for a slice in flight beside the
-        // operands)
-        if (kEarlyRefill)
-            issue(s, mslot);
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             const int o = row * kStgRow + 64 * i + 16 * grp;
@@ -1083,8 +1306,14 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
                 }
             }
         }
-        if (mt.last)
-            finish(mt);
+        if (mt.last) {
+            if (kEarlyRefill) {   // ended at the next segment's first block, or after the loop
+                fin_mt = mt;
+                pend_fin = true;
+            } else {
+                finish(mt);
+            }
+        }
         if (!kEarlyRefill)
             issue(s, mslot);
     };
@@ -1115,15 +1344,24 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
 #pragma unroll
     for (int i = 0; i < kSlots; ++i)
         nblk += mt[i].valid;
-    if (SRC == SRC_FUSED_DYNAMIC) {
+    nblk = __builtin_amdgcn_readfirstlane(nblk);   // wave-uniform: a scalar loop bound
+    if (SRC == SRC_FUSED_DYNAMIC)
         wk.ltp = wk.llen = nullptr;   // from here on the walker reads lengths from memory
-        __syncthreads();   // every wave is done with the LDS prefix, which the staging rows alias
-    }
+    // every wave is done with the LDS prefix (which the staging rows alias) and
+    // sees the cleared counters
+    __syncthreads();
     for (int it = 0; it < nblk; it += kSlots) {
         set_progress_priority(it, nblk);
 #pragma unroll
         for (int i = 0; i < kSlots; ++i)
             compute(sl[i], mt[i]);
+    }
+    if (kEarlyRefill && pend_fin)
+        finish(fin_mt);
+    if (NCB == 1) {
+        __syncthreads();   // every wave has posted its last segment
+        if (seg_idx > 0)
+            merge_held((seg_idx - 1) & (nbuf - 1), threadIdx.x, kDecodeThreads);
     }
 
     // single launch: arrive at the split pairs and merge those this workgroup
@@ -1171,24 +1409,33 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         }
         __syncthreads();
+        // the pairs to merge here: those whose counter this workgroup completed
         const int np = __builtin_amdgcn_readfirstlane(lds.npend);
-        for (int k = 0; k < np; ++k) {
-            if (!__builtin_amdgcn_readfirstlane(lds.pend_last[k]))
-                continue;
-            const int pb = __builtin_amdgcn_readfirstlane(lds.pend[k][0]);
-            const int pg = __builtin_amdgcn_readfirstlane(lds.pend[k][1]);
-            const int pn = __builtin_amdgcn_readfirstlane(lds.pend[k][2]);
-            const int wf = __builtin_amdgcn_readfirstlane(lds.pend[k][3]);
-            const int off = __builtin_amdgcn_readfirstlane(lds.pend[k][4]);
+        const int l0 = np > 0 && __builtin_amdgcn_readfirstlane(lds.pend_last[0]);
+        const int l1 = np > 1 && __builtin_amdgcn_readfirstlane(lds.pend_last[1]);
+        const int nm = l0 + l1;
+        // merge slot 0 is the first pending pair this workgroup completed, slot 1 the second
+        const int e0 = l0 ? 0 : 1;
+        int mn[2], mb[2], mg[2], mw[2], mo[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int e = k == 0 ? e0 : 1;
+            mb[k] = __builtin_amdgcn_readfirstlane(lds.pend[e][0]);
+            mg[k] = __builtin_amdgcn_readfirstlane(lds.pend[e][1]);
+            mn[k] = __builtin_amdgcn_readfirstlane(lds.pend[e][2]);
+            mw[k] = __builtin_amdgcn_readfirstlane(lds.pend[e][3]);
+            mo[k] = __builtin_amdgcn_readfirstlane(lds.pend[e][4]);
+        }
+        if (nm > 0) {
             const int sr = a.slot_rows;
             if (SRC == SRC_FUSED_DYNAMIC) {
-                merge_partials(a.part_o, a.part_lse, pn,
-                               [=](int s) { return (2 * (wf + s) + (s == 0 ? off : 0)) * sr; }, G, a.Hq, pb, pg,
-                               a.out, a.lse);
+                merge_pairs_at_end(a.part_o, a.part_lse, nm, mn, mb, mg,
+                                   [&](int k, int s) { return (2 * (mw[k] + s) + (s == 0 ? mo[k] : 0)) * sr; }, G,
+                                   a.Hq, a.out, a.lse);
             } else {
-                const int s0 = (pb * a.Hkv + pg) * a.S;
-                merge_partials(a.part_o, a.part_lse, pn, [=](int s) { return (s0 + s) * sr; }, G, a.Hq, pb, pg,
-                               a.out, a.lse);
+                merge_pairs_at_end(a.part_o, a.part_lse, nm, mn, mb, mg,
+                                   [&](int k, int s) { return ((mb[k] * a.Hkv + mg[k]) * a.S + s) * sr; }, G, a.Hq,
+                                   a.out, a.lse);
             }
         }
     }

@@ -4,37 +4,64 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <stdint.h>
 
 namespace vlkv {
 
-__device__ __forceinline__ int wave_incl_scan(int x)
+// Wave64 scans and reductions. Within each row of 16 lanes the running value
+// moves by DPP row shifts (1, 2, 4, 8: a lane whose source falls outside its
+// row keeps the identity); the rows are then joined through the row totals
+// (lanes 15, 31, 47, 63), read into scalar registers. No LDS traffic, so
+// each step costs a few cycles instead of a cross-lane permute's round trip.
+template <typename Op>
+__device__ __forceinline__ int row_incl_scan(int x, int id, Op op)
 {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off, 64);
-        if (lane >= off)
-            x += y;
-    }
+    x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x111, 0xf, 0xf, false));   // row_shr:1
+    x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x112, 0xf, 0xf, false));   // row_shr:2
+    x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x114, 0xf, 0xf, false));   // row_shr:4
+    x = op(x, __builtin_amdgcn_update_dpp(id, x, 0x118, 0xf, 0xf, false));   // row_shr:8
     return x;
 }
 
-__device__ __forceinline__ int wave_max(int x)
+template <typename Op>
+__device__ __forceinline__ int wave_incl_scan_op(int x, int id, Op op)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        x = max(x, __shfl_xor(x, off, 64));
-    return x;
+    x = row_incl_scan(x, id, op);
+    const int r0 = __builtin_amdgcn_readlane(x, 15);
+    const int r1 = __builtin_amdgcn_readlane(x, 31);
+    const int r2 = __builtin_amdgcn_readlane(x, 47);
+    const int row = (threadIdx.x & 63) >> 4;
+    const int c1 = r0, c2 = op(r0, r1), c3 = op(c2, r2);   // carries into rows 1, 2, 3
+    const int carry = row == 0 ? id : row == 1 ? c1 : row == 2 ? c2 : c3;
+    return op(carry, x);
 }
 
-__device__ __forceinline__ int wave_or(int x)
+// Reduction over the wave; the result is wave-uniform.
+template <typename Op>
+__device__ __forceinline__ int wave_reduce_op(int x, int id, Op op)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        x |= __shfl_xor(x, off, 64);
-    return x;
+    x = row_incl_scan(x, id, op);
+    const int r0 = __builtin_amdgcn_readlane(x, 15);
+    const int r1 = __builtin_amdgcn_readlane(x, 31);
+    const int r2 = __builtin_amdgcn_readlane(x, 47);
+    const int r3 = __builtin_amdgcn_readlane(x, 63);
+    return op(op(r0, r1), op(r2, r3));
 }
+
+struct OpAdd {
+    __device__ int operator()(int a, int b) const { return a + b; }
+};
+struct OpMax {
+    __device__ int operator()(int a, int b) const { return max(a, b); }
+};
+struct OpOr {
+    __device__ int operator()(int a, int b) const { return a | b; }
+};
+
+__device__ __forceinline__ int wave_incl_scan(int x) { return wave_incl_scan_op(x, 0, OpAdd{}); }
+__device__ __forceinline__ int wave_max(int x) { return wave_reduce_op(x, INT_MIN, OpMax{}); }
+__device__ __forceinline__ int wave_or(int x) { return wave_reduce_op(x, 0, OpOr{}); }
 
 // Exclusive prefix of one int per thread over a workgroup of NT threads (in
 // thread order); *total receives the sum over all threads. `lds` holds NT/64
@@ -104,13 +131,7 @@ __device__ __forceinline__ int block_excl_max_scan(int v, int lo, int *lds)
 {
     constexpr int NW = NT / 64;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    int incl = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off, 64);
-        if (lane >= off)
-            incl = max(incl, y);
-    }
+    const int incl = wave_incl_scan_op(v, INT_MIN, OpMax{});
     int excl = __shfl_up(incl, 1, 64);
     if (lane == 0)
         excl = lo;
