@@ -80,7 +80,7 @@ extern "C" {
  *   num_pages      physical pages in each cache
  *   pt_stride      row length of the page table (max pages per request)
  *   tile_tokens    T, the uniform tile; a multiple of 64
- *   num_wgs        W, workgroups of the decode launch (>= 1), or 0 for the
+ *   num_wgs        W, workgroups of the decode launch (1 .. 65536), or 0 for the
  *                  library default: a launch of 2 per compute unit of the
  *                  current device, of which the dynamic plan uses all when
  *                  that leaves at least 32 units (request, kv head, tile) per

@@ -95,8 +95,8 @@ static int check(const attn_shape *s, Shape *out)
     if (s->tile_tokens < kBlockTokens || s->tile_tokens % kBlockTokens)
         return fail(ATTN_ERR_UNSUPPORTED, "tile_tokens %d must be a positive multiple of %d",
                     s->tile_tokens, kBlockTokens);
-    if (s->num_wgs < 0 || s->num_wgs > (1 << 20))
-        return fail(ATTN_ERR_INVALID_ARG, "num_wgs %d outside [0, 2^20]", s->num_wgs);
+    if (s->num_wgs < 0 || s->num_wgs > (1 << 16))
+        return fail(ATTN_ERR_INVALID_ARG, "num_wgs %d outside [0, 2^16]", s->num_wgs);
     if (s->kv_dtype != ATTN_KV_BF16 && s->kv_dtype != ATTN_KV_FP8_E4M3)
         return fail(ATTN_ERR_UNSUPPORTED, "kv_dtype %d", s->kv_dtype);
     if (s->mode != ATTN_DYNAMIC && s->mode != ATTN_STATIC && s->mode != ATTN_SHARED)

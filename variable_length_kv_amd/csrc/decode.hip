@@ -231,9 +231,10 @@ struct Walker {
     int tpb;                 // tiles before request b
     int first_seg;           // the next segment entered is the workgroup's first
     int64_t N, We, u_beg, u_end;
+    UniformSplit split;   // the plan's cuts: begin(w) = floor(w N / We)
 
-    __device__ int64_t owner(int64_t u) const { return div_floor((u + 1) * We - 1, N); }
-    __device__ int64_t begin_of(int64_t ww) const { return div_floor(ww * N, We); }
+    __device__ int64_t owner(int64_t u) const { return split.owner((uint32_t)u); }
+    __device__ int64_t begin_of(int64_t ww) const { return split.begin((uint32_t)ww); }
 
     // single launch, dynamic: the prologue's LDS copies of the tiles prefix and
     // the validated lengths, used until the block loop starts (then nullptr)
@@ -307,6 +308,7 @@ struct Walker {
             } else {
                 N = N_;
                 We = We_;
+                split.init((uint32_t)N, (uint32_t)We);
                 u_beg = begin_of(w);
                 u_end = begin_of(w + 1);
                 u0 = (int)u_beg;

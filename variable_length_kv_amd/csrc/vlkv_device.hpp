@@ -171,6 +171,35 @@ __device__ __forceinline__ void block_max_or(int mx, int bits, int *lds, int *mx
     *bits_out = o;
 }
 
+// The uniform partition of N units into We contiguous ranges, range w being
+// [begin(w), begin(w + 1)) with begin(w) = floor(w N / We), for N < 2^31 and
+// 1 <= We <= 2^16, in 32-bit integer arithmetic: with N = qN We + rN,
+// begin(w) = w qN + floor(w rN / We), where w rN < 2^32.
+struct UniformSplit {
+    uint32_t N, We, qN, rN;
+    __device__ void init(uint32_t n, uint32_t we)
+    {
+        N = n;
+        We = we;
+        qN = n / we;
+        rN = n - qN * we;
+    }
+    __device__ uint32_t begin(uint32_t w) const { return w * qN + (w * rN) / We; }
+    // The range holding unit u < N: the largest w with begin(w) <= u. A
+    // single-precision estimate of u We / N (below 2^16, so off by less than
+    // one) is stepped to the answer.
+    __device__ uint32_t owner(uint32_t u) const
+    {
+        int w = (int)((float)u * ((float)We / (float)N));
+        w = w < 0 ? 0 : (w >= (int)We ? (int)We - 1 : w);
+        while (w + 1 < (int)We && begin(w + 1) <= u)
+            ++w;
+        while (w > 0 && begin(w) > u)
+            --w;
+        return (uint32_t)w;
+    }
+};
+
 // floor(x / d) for 0 <= x < 2^53, d > 0: double estimate, exact correction.
 __device__ __forceinline__ int64_t div_floor(int64_t x, int64_t d)
 {
