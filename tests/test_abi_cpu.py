@@ -63,6 +63,7 @@ def test_default_static_splits():
     (dict(page_size=24), L.ATTN_ERR_INVALID_ARG),
     (dict(tile_tokens=32), L.ATTN_ERR_UNSUPPORTED),
     (dict(num_wgs=-1), L.ATTN_ERR_INVALID_ARG),
+    (dict(num_wgs=65537), L.ATTN_ERR_INVALID_ARG),   # the plan's cuts use 32-bit products
     (dict(kv_dtype=7), L.ATTN_ERR_UNSUPPORTED),
     (dict(mode=3), L.ATTN_ERR_INVALID_ARG),
     (dict(num_pages=0), L.ATTN_ERR_INVALID_ARG),
