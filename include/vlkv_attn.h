@@ -175,7 +175,14 @@ int attn_plan(const attn_shape *shape, const int32_t *lengths, const int32_t *pa
               void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Decode attention over the plan in `workspace` (same stream).
+ * Decode attention over the plan in `workspace` (same stream): one query
+ * token per request against its paged, variable-length KV history, each
+ * workgroup streaming the uniform tiles the plan handed it and keeping a
+ * partial softmax state per (request, kv head) it touches [Tencent HPC lands
+ * in SGLang, challenging default inference kernels, sec. "Why Tencent HPC
+ * matters for online model serving": work cut into uniform tiles, partial
+ * results merged afterwards; KV in bf16 or fp8, sec. "What the 48.8% TPOT
+ * claim does not prove": cache precision as a benchmark dimension].
  *   q          (device) bf16 [B][Hq][D]
  *   k_cache    (device) [num_pages][Hkv][P][D], bf16 or uint8 e4m3fn codes
  *   v_cache    (device) same layout and dtype as k_cache
@@ -198,8 +205,12 @@ int attn_decode(const attn_shape *shape, const void *q, const void *k_cache,
 /*
  * Merge the partial results of (request, kv head) pairs that were split over
  * several workgroups (log-sum-exp weighting), and write o = 0, lse = -inf for
- * requests with L_b = 0. Must follow attn_decode on the same stream and
- * workspace. out, lse as in attn_decode.
+ * requests with L_b = 0 [Tencent HPC lands in SGLang, challenging default
+ * inference kernels, sec. "Why Tencent HPC matters for online model serving":
+ * the partial results of a request's tiles are combined after the tiles are
+ * processed]. Must follow attn_decode on the same stream and workspace. out,
+ * lse as in attn_decode. Each pair's partials are folded in slot order, so the
+ * result does not depend on timing.
  */
 int attn_combine(const attn_shape *shape, const void *workspace, size_t workspace_bytes,
                  void *out, float *lse, void *stream);
