@@ -58,6 +58,8 @@ typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
 typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
 typedef float f32x2 __attribute__((__vector_size__(2 * sizeof(float))));
 typedef short s16x4 __attribute__((__vector_size__(4 * sizeof(short))));
+typedef int i32x2 __attribute__((ext_vector_type(2)));      // LDS transpose loads' types
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kLdsRow = kHeadDim + 4;  // padded fp32 row of the merge buffer
@@ -144,21 +146,6 @@ __device__ __forceinline__ float xsum4(float x)
     x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
     auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Head dim held by output register i of accumulator block mb in row group grp.
-// bf16: block mb = 2*kk + s covers dims 32*kk + 16*s + [0,16) in order.
-// fp8 : lane (row, grp) loads dims 16*(grp + 4p) + [0,16) for p = 0,1; the
-//       selection MFMA (p, h, s) with columns n then yields
-//       dim 64p + 32s + 16*(n/8) + 8h + n%8 for block mb = 4p + 2h + s.
-template <int KVFP8>
-__device__ __forceinline__ int out_dim(int mb, int c)
-{
-    if (KVFP8) {
-        const int p = mb >> 2, h = (mb >> 1) & 1, s = mb & 1;
-        return 64 * p + 32 * s + 16 * (c >> 3) + 8 * h + (c & 7);
-    }
-    return 16 * mb + c;
 }
 
 // Validated length of request b as the planner defines it: L_b if
@@ -727,22 +714,6 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
         }
     }
 
-    // 0/1 selection matrices for the in-register V transpose: B operand, lane
-    // (n = row, grp) element j stands for k = 8*grp + j; Sel_s[k][n] = (k == n + 16 s)
-    bf16x8 sel16[2];
-    uint64_t sel8[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        uint64_t bits = 0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const bool one = 8 * grp + j == row + 16 * s;
-            sel16[s][j] = one ? (__bf16)1.0f : (__bf16)0.0f;
-            bits |= (uint64_t)(one ? 0x38u : 0u) << (8 * j);  // e4m3fn 1.0 = 0x38
-        }
-        sel8[s] = bits;
-    }
-
     Walker<SRC, kBT> wk;
     wk.init(&a, w, wave, lds.tp, lds.len, N, We, chunk);
 
@@ -928,15 +899,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
                 }
                 float *ar = acc_row(buf, wave, rr);
 #pragma unroll
-                for (int mb = 0; mb < 8; ++mb) {
-                    if (KVFP8) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            ar[out_dim<1>(mb, 4 * pgrp + i)] = acc[cb][mb][i];
-                    } else {
-                        *reinterpret_cast<f32x4 *>(ar + 16 * mb + 4 * pgrp) = acc[cb][mb];
-                    }
-                }
+                for (int mb = 0; mb < 8; ++mb)
+                    *reinterpret_cast<f32x4 *>(ar + 16 * mb + 4 * pgrp) = acc[cb][mb];
             }
         }
     };
@@ -1113,10 +1077,9 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
         const Meta mcopy = mslot;   // the slot's description is replaced by the refill
         const Meta &mt = kEarlyRefill ? mcopy : mslot;
         constexpr int NL = 4;
-        // operand registers: the slot's own once it is not refilled before the math
-        u32x4 kbuf[4], vbuf[4];
+        // K operand registers: the slot's own once it is not refilled before the math
+        u32x4 kbuf[4];
         u32x4(&kop)[4] = kEarlyRefill ? kbuf : s.k;
-        u32x4(&vop)[4] = kEarlyRefill ? vbuf : s.v;
         // Load i of lane l brought slice bytes [1024 i + 16 l, +16): staged row
         // (1024 i + 16 l) / 256, column byte (1024 i + 16 l) % 256 (a staged row
         // is one bf16 cache row, or two fp8 cache rows). Write them to this
@@ -1179,7 +1142,6 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
         for (int i = 0; i < NL; ++i) {
             const int o = row * kStgRow + 64 * i + 16 * grp;
             kop[i] = *reinterpret_cast<const u32x4 *>(sk + o);
-            vop[i] = *reinterpret_cast<const u32x4 *>(sv + o);
         }
         {
             // Scores S^T[sub-tile row 4*grp+i][head row], per column block and
@@ -1270,40 +1232,49 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
                 }
             }
             // rows past the length were read as zeros (the loads' range ends at
-            // the last valid row), so they add nothing to P.V
-            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            // the last valid row), so they add nothing to P.V.
+            // V^T, the A operand of P.V, is read from the staged V rows by
+            // LDS transpose loads: in each 16-lane row group, lane 8h + c (tr_b8)
+            // or 4h + c (tr_b16) receives element c of the 8-byte chunks that
+            // lanes 2j + h (j = 0..7) or 4j + h (j = 0..3) address. Lane (16 g +
+            // i) addresses the chunk of V[token of its group's reduction index
+            // j][dims 16 mb + 8h .. or 4h ..], so that lane (16 g + d) receives
+            // V[token(g, j)][16 mb + d], j = 0.. in the reduction order of P^T:
+            // bf16, token 4g + j; fp8, the token of sub-tile j / 4, row
+            // 4g + j % 4 (token 2 (4g + j % 4) + j / 4 of the staged row pairs).
+            {
+                const int gi = lane & 15;
+                int vrow;
+                if (KVFP8) {
+                    const int j = gi >> 1, h = gi & 1;
+                    vrow = (4 * grp + (j & 3)) * kStgRow + (j >> 2) * 128 + 8 * h;
+                } else {
+                    const int j = gi >> 2, h = gi & 3;
+                    vrow = (4 * grp + j) * kStgRow + 8 * h;
+                }
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-                for (int ss = 0; ss < 2; ++ss) {
+                for (int mb = 0; mb < 8; ++mb) {
                     if (KVFP8) {
-                        // V^T of both sub-tiles side by side is the A operand of a
-                        // 32-deep product: lane l holds reduction index 8*grp + j,
-                        // the token of sub-tile j / 4, row 4*grp + j % 4; the two
-                        // sub-tiles' P^T side by side is the B operand in that order
-                        s16x4 vt[2];
-#pragma unroll
-                        for (int sub = 0; sub < 2; ++sub) {
-                            const u32x2 src = {vop[2 * sub + (kk >> 1)][2 * (kk & 1)],
-                                               vop[2 * sub + (kk >> 1)][2 * (kk & 1) + 1]};
-                            vt[sub] = pack_bf16x4(__builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
-                                __builtin_bit_cast(long, src), (long)sel8[ss], zero, 0, 0, 0));
-                        }
-                        const bf16x8 va = cat_bf16x8(vt[0], vt[1]);
+                        const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                            (__attribute__((address_space(3))) i32x2 *)(sv + vrow + 16 * mb));
+                        const bf16x2 c0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[0], 1.0f, false);
+                        const bf16x2 c1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[0], 1.0f, true);
+                        const bf16x2 c2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[1], 1.0f, false);
+                        const bf16x2 c3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[1], 1.0f, true);
+                        const bf16x8 va = bf16x8{c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
 #pragma unroll
                         for (int cb = 0; cb < NCB; ++cb)
                             if (cb == 0 || two)
-                                acc[cb][2 * kk + ss] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                    va, cat_bf16x8(pb[cb][0], pb[cb][NST - 1]), acc[cb][2 * kk + ss], 0, 0, 0);
+                                acc[cb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    va, cat_bf16x8(pb[cb][0], pb[cb][NST - 1]), acc[cb][mb], 0, 0, 0);
                     } else {
-                        const f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vop[kk]),
-                                                                                sel16[ss], zero, 0, 0, 0);
-                        const s16x4 vt = pack_bf16x4(t);
+                        const s16x4 vt = __builtin_bit_cast(s16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) i16x4 *)(sv + vrow + 32 * mb)));
 #pragma unroll
                         for (int cb = 0; cb < NCB; ++cb)
                             if (cb == 0 || two)
-                                acc[cb][2 * kk + ss] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                                    vt, pb[cb][0], acc[cb][2 * kk + ss], 0, 0, 0);
+                                acc[cb][mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pb[cb][0], acc[cb][mb], 0, 0,
+                                                                                          0);
                     }
                 }
             }
