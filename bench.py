@@ -621,7 +621,8 @@ def trace_leg(torch, L, W_of, flush, steps=256):
 def traffic_probe(torch, L, W, reps=3):
     """Launches for rocprofv3 --pmc runs: a plain 1 GiB device copy (the
     counter scale), then the headline step, single-launch and three-launch,
-    each `reps` times, with a cache flush before each launch."""
+    each `reps` times, then the single launch on an fp8 e4m3 copy of the same
+    batch `reps` times, with a cache flush before each launch."""
     from variable_length_kv_amd import workloads as wl
     flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
     src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
@@ -638,8 +639,16 @@ def traffic_probe(torch, L, W, reps=3):
             flush.sum()
             r.step(att, fused)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes": src.numel() * 4, "decode_kv_bytes": c1.kv_bytes, "reps": reps,
-                      "source_hash": source_hash()}), flush=True)
+    del att, r
+    c8 = wl.make_case("uniform_mixed_fp8", c1.lengths, Hq=c1.Hq, Hkv=c1.Hkv, P=c1.P, kv_dtype="fp8")
+    r8 = Runner(c8, torch, L, W)
+    att8 = r8.attention(L.ATTN_DYNAMIC)
+    for _ in range(reps):
+        flush.sum()
+        r8.step(att8, True)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": src.numel() * 4, "decode_kv_bytes": c1.kv_bytes,
+                      "decode_kv_bytes_fp8": c8.kv_bytes, "reps": reps, "source_hash": source_hash()}), flush=True)
 
 
 def router_probe(torch, L, reps=3):

@@ -63,7 +63,11 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kLdsRow = kHeadDim + 4;  // padded fp32 row of the merge buffer
-constexpr int kStgRow = kHeadDim * 2 + 16;  // padded byte row of a staged K or V slice
+// A staged K or V row: 256 bytes of data (one bf16 cache row, or two fp8 cache
+// rows with a 16-byte gap between them) padded to 288 bytes, which keeps the
+// row-strided operand reads and the transpose loads on distinct LDS banks.
+constexpr int kStgRow = kHeadDim * 2 + 32;
+constexpr int kFp8HalfGap = 16;   // offset of an fp8 staged row's second cache row: 128 + 16
 constexpr float kLazy = 8.f;           // lazy-rescale threshold (log2 units)
 constexpr int kMergeBatch = 4;         // partials folded together by the LSE merge
 constexpr int kMailboxSpin = 1 << 22;  // bound of a mailbox wait (s_sleep 1 each, ~0.1 s)
@@ -438,6 +442,18 @@ struct Walker {
 __device__ __forceinline__ void store_coherent(float *p, float x)
 {
     __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Four consecutive floats base[i .. i+3] with the same cache policy as
+// store_coherent (sc1: written through to the device's coherence point), as
+// one 16-byte store: the per-float stores would each be a separate partial
+// write of a memory line. `base` is wave-uniform (a buffer descriptor) and
+// 0 <= i < 2^29.
+constexpr int kStoreSc1 = 16;   // cache-policy bit sc1 of a buffer store (gfx950)
+__device__ __forceinline__ void store_coherent4(float *base, int i, f32x4 x)
+{
+    const auto r = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, kRsrcWord3);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, i * (int)sizeof(float), 0, kStoreSc1);
 }
 
 // The LSE merge of partial results (o normalised, lse in base 2) of one
@@ -950,10 +966,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
                 if (a.lse && d4 == 0)
                     a.lse[hq] = lse2 * kLn2;
             } else if (kFused) {
-                float *po = a.part_o + prow * D + d4;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    store_coherent(po + i, o[i]);
+                // (the slot's rows start at a wave-uniform address)
+                store_coherent4(a.part_o + (size_t)mt.slot * a.slot_rows * D, h * D + d4, o);
                 if (d4 == 0)
                     store_coherent(a.part_lse + prow, lse2);
             } else {
@@ -1082,17 +1096,18 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
         u32x4(&kop)[4] = kEarlyRefill ? kbuf : s.k;
         // Load i of lane l brought slice bytes [1024 i + 16 l, +16): staged row
         // (1024 i + 16 l) / 256, column byte (1024 i + 16 l) % 256 (a staged row
-        // is one bf16 cache row, or two fp8 cache rows). Write them to this
-        // wave's staging rows, then read back the operand layout (row = lane %
-        // 16, bytes 64 i + 16 * (lane / 16)). LDS operations of one wave
-        // complete in order, so no barrier is needed.
+        // is one bf16 cache row, or two fp8 cache rows, the second kFp8HalfGap
+        // bytes after the first's end). Write them to this wave's staging rows,
+        // then read back the operand layout (row = lane % 16, bytes 64 i + 16 *
+        // (lane / 16)). LDS operations of one wave complete in order, so no
+        // barrier is needed.
         constexpr int RB = 256;
         uint8_t *sk = lds.r.stg[wave][0];
         uint8_t *sv = lds.r.stg[wave][1];
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             const int byte = 1024 * i + 16 * lane;
-            const int o = (byte / RB) * kStgRow + byte % RB;
+            const int o = (byte / RB) * kStgRow + byte % RB + (KVFP8 && byte % RB >= RB / 2 ? kFp8HalfGap : 0);
             *reinterpret_cast<u32x4 *>(sk + o) = s.k[i];
             *reinterpret_cast<u32x4 *>(sv + o) = s.v[i];
         }
@@ -1140,7 +1155,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
         }
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
-            const int o = row * kStgRow + 64 * i + 16 * grp;
+            const int o = row * kStgRow + 64 * i + 16 * grp + (KVFP8 && i >= NL / 2 ? kFp8HalfGap : 0);
             kop[i] = *reinterpret_cast<const u32x4 *>(sk + o);
         }
         {
@@ -1247,7 +1262,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
                 int vrow;
                 if (KVFP8) {
                     const int j = gi >> 1, h = gi & 1;
-                    vrow = (4 * grp + (j & 3)) * kStgRow + (j >> 2) * 128 + 8 * h;
+                    vrow = (4 * grp + (j & 3)) * kStgRow + (j >> 2) * (128 + kFp8HalfGap) + 8 * h;
                 } else {
                     const int j = gi >> 2, h = gi & 3;
                     vrow = (4 * grp + j) * kStgRow + 8 * h;
