@@ -31,6 +31,7 @@ WRITE_DIR PROBE_OUTPUT OUT_JSON (rocprofv3 output directories, see profiles/).
 """
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -58,11 +59,25 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+_CODE_TOKENS = re.compile(r'"(?:\\.|[^"\\\n])*"'      # string literal
+                          r"|'(?:\\.|[^'\\\n])*'"       # character literal
+                          r"|//[^\n]*"                       # line comment
+                          r"|/\*.*?\*/"                     # block comment
+                          r"|\S+?(?=//|/\*|[\s\"']|$)"     # any other run of code
+                          r"|\S", re.S)
+
+
 def source_hash():
+    """Hash of the decode kernels' code, blind to comments and to the width of
+    whitespace, so a profile taken before a comment-only edit still matches
+    the kernel."""
     h = hashlib.sha256()
     for f in ("decode.hip", "vlkv_internal.hpp", "vlkv_device.hpp"):
-        with open(os.path.join(ROOT, "variable_length_kv_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "variable_length_kv_amd", "csrc", f), encoding="utf-8") as fh:
+            text = fh.read()
+        for tok in _CODE_TOKENS.findall(text):
+            if not tok.startswith(("//", "/*")):
+                h.update(tok.encode() + b"\0")
     return h.hexdigest()[:16]
 
 

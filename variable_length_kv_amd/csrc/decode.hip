@@ -12,38 +12,38 @@
 // workgroup to finish a split (request, kv head) pair merges its partials,
 // after its own blocks.
 //
-// Workgroup = 4 wave64s. A 64-token block of one (request b, kv head g) is split
-// into four 16-token slices, one per wave; every wave walks the same sequence of
-// blocks, keeps its own online-softmax state for the G query heads of g, and the
-// four states are merged through LDS at the end of each segment.
+// Workgroup = 4 wave64s. A block of one (request b, kv head g), 64 tokens for a
+// bf16 cache and 128 for fp8, is split into four slices, one per wave: 16 bf16
+// or 32 fp8 cache rows, 4 KB of K and 4 KB of V either way. Every wave walks the
+// same sequence of blocks and keeps its own online-softmax state for the G query
+// heads of g; the four states are merged through LDS at the end of each segment.
 //
-// Per wave and slice (16 tokens x 128 dims of K and of V):
-//   * The slice's K and V rows (4 KB each for bf16, 2 KB for fp8, contiguous
-//     in the page) are read with 16-byte non-temporal loads, lane l taking
-//     bytes 16 l + 1024 i of load i: each load instruction reads 1 KB of whole
-//     128-byte lines, and the lines are not kept in the caches (every K/V byte
-//     is read once per step). Two slices per wave are in flight in registers
-//     on top of two resident waves per SIMD.
+// Per wave and slice:
+//   * The slice's K and V rows (contiguous in the page) are read by raw buffer
+//     loads through descriptors whose range is exactly the slice's valid rows,
+//     lane l taking bytes 16 l + 1024 i of load i: each instruction reads 1 KB
+//     of whole 128-byte lines, non-temporally (every K/V byte is read once per
+//     step). Two slices per wave are in flight in registers, on top of two
+//     resident waves per SIMD.
 //   * At the slice's compute the wave writes its registers to its own LDS
-//     staging rows and reads back the MFMA operand layout: lane l holds token
-//     row l%16 and a run of dims selected by l/16. Loading that layout straight
-//     from memory reads 64 bytes of each of 16 rows per instruction, half
-//     lines that a non-temporal load would fetch twice; through LDS the loads
-//     stream at the rate of contiguous reads. The staging rows share LDS with
-//     the segment-end merge buffer; a barrier before each merge separates the
-//     two uses.
-//   * S^T = K Q^T with 4 bf16 MFMAs 16x16x32 (16 tokens x 16 heads; heads >= G
-//     are zero). fp8 K codes are widened to bf16 exactly first. The result's
-//     lane layout (lane l: tokens 4*(l/16)+i, head l%16) is exactly the B
-//     operand of the 16x16x16 bf16 MFMA, so P^T needs no data movement.
+//     staging rows and reads back the K operand layout (lane l: token row l%16,
+//     a run of dims selected by l/16). Loading that layout straight from memory
+//     reads 64 bytes of each of 16 rows per instruction, half lines that a
+//     non-temporal load would fetch twice; through LDS the loads stream at the
+//     rate of contiguous reads.
+//   * S^T = K Q^T with bf16 MFMAs 16x16x32 (16 tokens x 16 query rows; rows >= G
+//     are zero): one 16-token sub-tile for bf16, two for fp8, whose codes are
+//     widened to bf16 exactly first. The result's lane layout (lane l: tokens
+//     4*(l/16)+i, query row l%16) is the B operand of the P.V MFMA, so P^T needs
+//     no data movement.
 //   * Online softmax in base 2 (sm_scale*log2 e, times the fp8 k scale, folded
-//     into one multiply); per-head maxima across the 4 lane groups by permlane
-//     swaps.
-//   * V is transposed in registers by an MFMA against a 0/1 selection matrix:
-//     D = V_rows x Sel gives, in lane l, V[token 4*(l/16)+i][one dim per l%16],
-//     which is the A operand (V^T) of the 16x16x16 bf16 MFMA. The product is
-//     exact (one nonzero term), so it also widens fp8 codes to bf16 for free.
-//   * O^T (128 dims x 16 heads) += V^T P^T with 8 MFMAs into 32 fp32 registers.
+//     into one multiply); per-row maxima across the 4 lane groups by permlane
+//     swaps; the reference maximum moves only when it is exceeded by more than
+//     kLazy.
+//   * V^T, the A operand of P.V, is read from the staged V rows by LDS transpose
+//     loads (16-bit or 8-bit elements), fp8 codes widened to bf16 after them.
+//   * O^T (128 dims x 16 query rows) += V^T P^T with 8 MFMAs into 32 fp32
+//     registers.
 #include "vlkv_device.hpp"
 #include "vlkv_internal.hpp"
 
@@ -62,7 +62,7 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));      // LDS transpose loa
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kLdsRow = kHeadDim + 4;  // padded fp32 row of the merge buffer
+constexpr int kLdsRow = kHeadDim + 4;  // padded fp32 row of the segment-end mailbox
 // A staged K or V row: 256 bytes of data (one bf16 cache row, or two fp8 cache
 // rows with a 16-byte gap between them) padded to 288 bytes, which keeps the
 // row-strided operand reads and the transpose loads on distinct LDS banks.
