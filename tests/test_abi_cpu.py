@@ -12,9 +12,14 @@ from variable_length_kv_amd import lib as L
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _declared():
+DEBUG_HEADER = "vlkv_attn_debug.h"
+
+
+def _declared(debug=False):
     names = set()
     for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        if (os.path.basename(h) == DEBUG_HEADER) != debug:
+            continue
         src = open(h).read()
         src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
         names |= set(re.findall(r"\b((?:attn|router)_[a-z_0-9]+)\s*\(", src))
@@ -28,6 +33,20 @@ def test_library_exports_every_declared_symbol():
     assert declared == set(L.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
+    for name in L.DEBUG_EXPORTED:   # the counting entry is in the visit-counting build only
+        assert not hasattr(lib, name), name
+
+
+def test_visit_counting_build_exports_the_same_plus_its_entry():
+    lib = ctypes.CDLL(L.VISITS_LIB_PATH)
+    debug = _declared(debug=True)
+    assert debug == set(L.DEBUG_EXPORTED)
+    for name in _declared() | debug:
+        assert hasattr(lib, name), name
+    dbg = L.load_visits()
+    # pointer and stride must agree; checked on the host before any HIP call
+    assert dbg.attn_debug_visits(None, 8, None) == L.ATTN_ERR_INVALID_ARG
+    assert dbg.attn_debug_visits(ctypes.c_void_p(256), 0, None) == L.ATTN_ERR_INVALID_ARG
 
 
 def _shape(**kw):

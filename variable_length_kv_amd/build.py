@@ -1,8 +1,10 @@
 """Build libvlkv_attn.so in-tree with hipcc for gfx950.
 
 ``python -m variable_length_kv_amd.build`` compiles every HIP source under
-``csrc/`` into one shared library next to this file. All device code is built
-without packed-FP32 instructions (``-packed-fp32-ops``).
+``csrc/`` into one shared library next to this file, and the same sources with
+``VLKV_DEBUG_VISITS`` defined into libvlkv_attn_visits.so, the visit-counting
+build that the work-list tests load (include/vlkv_attn_debug.h). All device
+code is built without packed-FP32 instructions (``-packed-fp32-ops``).
 """
 import os
 import shutil
@@ -12,6 +14,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libvlkv_attn.so")
+VISITS_LIB = os.path.join(HERE, "libvlkv_attn_visits.so")
 SOURCES = ["plan.hip", "decode.hip", "append.hip", "router.hip", "api.hip"]
 ARCH = "gfx950"
 
@@ -29,19 +32,32 @@ def flags():
             "-I", os.path.join(HERE, "..", "include")]
 
 
-def build(verbose: bool = False, extra=()) -> str:
+def build(verbose: bool = False, extra=(), visits: bool = True) -> str:
+    """Compile the library (and, with ``visits``, its visit-counting build,
+    in a second hipcc process at the same time); returns the library's path."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    cmd = [hipcc()] + flags() + list(extra) + ["-shared", "-o", LIB + ".tmp"] + srcs
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
-                     if "packed-fp32-ops" not in l and l.strip())
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + msgs)
-    if verbose and msgs:
-        print(msgs, file=sys.stderr)
-    os.replace(LIB + ".tmp", LIB)
+    jobs = [(LIB, list(extra))]
+    if visits:
+        # -Bsymbolic: its own calls bind inside it when both libraries are loaded
+        jobs.append((VISITS_LIB, list(extra) + ["-DVLKV_DEBUG_VISITS", "-Wl,-Bsymbolic"]))
+    procs = []
+    for out, ex in jobs:
+        cmd = [hipcc()] + flags() + ex + ["-shared", "-o", out + ".tmp"] + srcs
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((out, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+    failed = []
+    for out, p in procs:
+        text, _ = p.communicate()
+        msgs = "\n".join(l for l in text.splitlines() if "packed-fp32-ops" not in l and l.strip())
+        if p.returncode != 0:
+            failed.append(f"hipcc failed for {os.path.basename(out)}:\n{msgs}")
+            continue
+        if verbose and msgs:
+            print(msgs, file=sys.stderr)
+        os.replace(out + ".tmp", out)
+    if failed:
+        raise RuntimeError("\n".join(failed))
     return LIB
 
 

@@ -9,6 +9,9 @@
 #include <string>
 
 #include "../../include/vlkv_attn.h"
+#ifdef VLKV_DEBUG_VISITS
+#include "../../include/vlkv_attn_debug.h"
+#endif
 #include "vlkv_internal.hpp"
 
 namespace vlkv {
@@ -684,6 +687,20 @@ int attn_append_kv(const attn_shape *shape, const void *k_new, const void *v_new
         return hip_fail(e, "append launch");
     return ok();
 }
+
+#ifdef VLKV_DEBUG_VISITS
+int attn_debug_visits(int32_t *tok_counts, int64_t tok_stride, int32_t *out_counts)
+{
+    if ((tok_counts != nullptr) != (tok_stride > 0))
+        return fail(ATTN_ERR_INVALID_ARG, "tok_counts needs tok_stride > 0 (and null needs 0)");
+    hipError_t e = hipDeviceSynchronize();   // no kernel of an earlier step still counts
+    if (e == hipSuccess)
+        e = set_debug_visits(tok_counts, tok_stride, out_counts);
+    if (e != hipSuccess)
+        return hip_fail(e, "visit counters");
+    return ok();
+}
+#endif
 
 int attn_get_status(const void *workspace, uint32_t *flags, void *stream)
 {

@@ -79,6 +79,24 @@ constexpr int kLoadNT = 2;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+#ifdef VLKV_DEBUG_VISITS
+// Counters of the visit-counting build (see set_debug_visits).
+struct DebugVisits {
+    int32_t *tok, *out;
+    int64_t tok_stride;
+};
+__device__ DebugVisits g_visits;
+
+__device__ __forceinline__ void debug_count_out(size_t hq, int d4)
+{
+    if (g_visits.out && d4 == 0)
+        atomicAdd(g_visits.out + hq, 1);
+}
+#define VLKV_COUNT_OUT(hq, d4) debug_count_out(hq, d4)
+#else
+#define VLKV_COUNT_OUT(hq, d4) ((void)0)
+#endif
+
 // Wave priority from a workgroup's progress through its blocks: 3 for the
 // first half, 2 up to 80%, 1 up to 95%, 0 for the rest. Two workgroups share a
 // CU, and among ready waves of equal priority the SIMD issues the older one
@@ -502,6 +520,7 @@ __device__ __forceinline__ void merge_write(float M, float den, f32x4 o, uint16_
     *reinterpret_cast<bf16x4 *>(out + hq * kHeadDim + d4) = __builtin_convertvector(o, bf16x4);
     if (lse && d4 == 0)
         lse[hq] = lse2 * kLn2;
+    VLKV_COUNT_OUT(hq, d4);
 }
 
 // Merge n partials of one (request, kv head) pair into the bf16 output and the
@@ -716,6 +735,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
                     *reinterpret_cast<bf16x4 *>(a.out + hq * D + d4) = bf16x4{0, 0, 0, 0};
                     if (a.lse && d4 == 0)
                         a.lse[hq] = -INFINITY;
+                    VLKV_COUNT_OUT(hq, d4);
                 }
             }
             if (w >= We)
@@ -965,6 +985,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
                 *reinterpret_cast<bf16x4 *>(a.out + hq * D + d4) = ob;
                 if (a.lse && d4 == 0)
                     a.lse[hq] = lse2 * kLn2;
+                VLKV_COUNT_OUT(hq, d4);
             } else if (kFused) {
                 // (the slot's rows start at a wave-uniform address)
                 store_coherent4(a.part_o + (size_t)mt.slot * a.slot_rows * D, h * D + d4, o);
@@ -1090,6 +1111,15 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeArgs a)
     auto compute = [&](Slot &s, Meta &mslot) {
         const Meta mcopy = mslot;   // the slot's description is replaced by the refill
         const Meta &mt = kEarlyRefill ? mcopy : mslot;
+#ifdef VLKV_DEBUG_VISITS
+        // lane j: the slice's row j, for each request the block serves
+        if (g_visits.tok && lane < mt.nv) {
+            const int64_t j = (int64_t)mt.tbase + mt.tok0 + lane;
+            for (int r = 0; r < mt.m; ++r)
+                if (j < g_visits.tok_stride)
+                    atomicAdd(g_visits.tok + ((int64_t)(mt.b + r) * a.Hkv + mt.g) * g_visits.tok_stride + j, 1);
+        }
+#endif
         constexpr int NL = 4;
         // K operand registers: the slot's own once it is not refilled before the math
         u32x4 kbuf[4];
@@ -1522,6 +1552,14 @@ hipError_t launch_combine(const CombineArgs &a, hipStream_t st)
         hipLaunchKernelGGL(combine_kernel, dim3(grid), dim3(kDecodeThreads), 0, st, a);
     return hipGetLastError();
 }
+
+#ifdef VLKV_DEBUG_VISITS
+hipError_t set_debug_visits(int32_t *tok, int64_t tok_stride, int32_t *out)
+{
+    const DebugVisits v{tok, out, tok_stride};
+    return hipMemcpyToSymbol(HIP_SYMBOL(g_visits), &v, sizeof(v));
+}
+#endif
 
 hipError_t launch_ws_init(int32_t *header, int32_t *counters, int n_counters, hipStream_t st)
 {

@@ -132,4 +132,12 @@ hipError_t launch_decode(const DecodeArgs &a, int src, int kv_fp8, int grid, hip
 hipError_t launch_combine(const CombineArgs &a, hipStream_t st);
 hipError_t launch_ws_init(int32_t *header, int32_t *counters, int n_counters, hipStream_t st);
 
+#ifdef VLKV_DEBUG_VISITS
+// Visit-counting build only: every decode and combine kernel adds 1 to
+// tok[(b * Hkv + g) * tok_stride + j] for each cached row j of request b, kv
+// head g that its attention math consumes, and 1 to out[b * Hq + h] for each
+// write of a final output row (null pointers: nothing is counted).
+hipError_t set_debug_visits(int32_t *tok, int64_t tok_stride, int32_t *out);
+#endif
+
 }  // namespace vlkv

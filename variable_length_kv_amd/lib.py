@@ -8,6 +8,7 @@ no fallback implementation.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from dataclasses import dataclass
@@ -16,6 +17,8 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libvlkv_attn.so")
+# the visit-counting build of the same sources (include/vlkv_attn_debug.h)
+VISITS_LIB_PATH = os.path.join(_HERE, "libvlkv_attn_visits.so")
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
 ATTN_KV_BF16, ATTN_KV_FP8_E4M3 = 0, 1
@@ -27,6 +30,7 @@ EXPORTED = ("attn_check_shape", "attn_workspace_bytes", "attn_static_splits", "a
             "attn_workspace_init", "attn_step", "attn_step_noalloc", "attn_append_kv", "attn_read_plan_items",
             "attn_last_error",
             "router_split_weights", "router_workspace_bytes", "router_gemm")
+DEBUG_EXPORTED = ("attn_debug_visits",)   # libvlkv_attn_visits.so only
 
 
 class AttnError(RuntimeError):
@@ -63,16 +67,21 @@ class AttnShape:
 
 
 _lib = None
+_visits_lib = None
 
 
 def load():
     """Load libvlkv_attn.so (raises if it is not built)."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m variable_length_kv_amd.build`")
-    lib = ctypes.CDLL(LIB_PATH)
+    if _lib is None:
+        _lib = _open(LIB_PATH)
+    return _lib
+
+
+def _open(path, debug=False):
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m variable_length_kv_amd.build`")
+    lib = ctypes.CDLL(path)
     P, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     SP = ctypes.POINTER(_Shape)
     sigs = {
@@ -96,12 +105,45 @@ def load():
         "router_gemm": (i32, [i32, i32, i32, P, P, P, P, P, sz, P]),
         "attn_last_error": (ctypes.c_char_p, []),
     }
+    if debug:
+        sigs["attn_debug_visits"] = (i32, [P, ctypes.c_int64, P])
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    _lib = lib
     return lib
+
+
+def load_visits():
+    """Load the visit-counting build libvlkv_attn_visits.so (raises if it is not built)."""
+    global _visits_lib
+    if _visits_lib is None:
+        _visits_lib = _open(VISITS_LIB_PATH, debug=True)
+    return _visits_lib
+
+
+@contextlib.contextmanager
+def counting_visits(tok_counts, tok_stride, out_counts):
+    """Route every call of this module through the visit-counting build while
+    the block runs, with its counters set to the given int32 device tensors
+    (tok_counts [B][Hkv][tok_stride], out_counts [B][Hq]; see
+    include/vlkv_attn_debug.h). Workspaces made by either build serve both."""
+    global _lib
+    dbg = load_visits()
+    saved = load()
+    _on_gpu(tok_counts=tok_counts, out_counts=out_counts)
+    _check_with(dbg, dbg.attn_debug_visits(_ptr(tok_counts), int(tok_stride), _ptr(out_counts)))
+    _lib = dbg
+    try:
+        yield
+    finally:
+        _lib = saved
+        _check_with(dbg, dbg.attn_debug_visits(None, 0, None))
+
+
+def _check_with(lib, rc):
+    if rc != ATTN_OK:
+        raise AttnError(rc, lib.attn_last_error().decode())
 
 
 def _check(rc):
