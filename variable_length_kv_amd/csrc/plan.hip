@@ -31,8 +31,8 @@
 // The work is O(B*Hkv + W) and latency-bound: each thread owns a contiguous
 // chunk of every array, so a prefix sum is one serial pass per thread, one
 // wave scan and one exchange of 4 wave totals through LDS. Mode 2 adds the
-// page-table comparison of adjacent requests: 256 slots per coalesced wave
-// step, 8 requests in flight in each of 16 waves.
+// page-table comparison of adjacent requests: 4 consecutive requests per wave
+// (16 waves) at a time, their 5 rows loaded once, 256 slots per row and step.
 #include "vlkv_device.hpp"
 #include "vlkv_internal.hpp"
 
@@ -41,8 +41,8 @@ namespace {
 
 constexpr int kPT = 256;  // planner threads
 constexpr int kPW = kPT / 64;
-constexpr int kST = 1024; // threads of the prefix-shared planner: more waves keep more
-constexpr int kSW = kST / 64;   // page-table loads in flight (each wave holds at most 63)
+constexpr int kST = 1024; // threads of the prefix-shared planner
+constexpr int kSW = kST / 64;
 
 // The dynamic partition over n "items" (requests in modes 0, items in mode
 // 2) whose tiles prefix is tp[0..n]: segments of each (item, kv head) pair and
@@ -53,34 +53,39 @@ __device__ void plan_partition(const PlanArgs &a, const int32_t *tp, int n, int 
 {
     const int tid = threadIdx.x;
     int run;
-    // segments per (item, g) and their prefix
+    // segments per (item, g) and their prefix. The owner of unit u,
+    // floor(((u + 1) We - 1) / N), is the largest w with begin(w) <= u: the
+    // 32-bit uniform split computes both (N < 2^31 and We <= 2^16 by the
+    // shape checks).
     const int nbg = n * a.Hkv;
     const int64_t N = (int64_t)total * a.Hkv;
     const int64_t We = plan_wgs(N, a.W, a.W_auto);
+    UniformSplit split;
+    if (We > 0)
+        split.init((uint32_t)N, (uint32_t)We);
     const int cB = (nbg + NT - 1) / NT;
     const int g0 = min(nbg, tid * cB), g1 = min(nbg, g0 + cB);
     int segs = 0;
     for (int bg = g0; bg < g1; ++bg) {
         const int b = bg / a.Hkv, g = bg - b * a.Hkv;
-        const int64_t nb = tp[b + 1] - tp[b];
+        const int nb = tp[b + 1] - tp[b];
         if (nb == 0) {
             a.first_wg[bg] = -1;
         } else {
-            const int64_t u0 = (int64_t)tp[b] * a.Hkv + g * nb;
-            const int64_t w0 = div_floor((u0 + 1) * We - 1, N);
-            const int64_t w1 = div_floor((u0 + nb) * We - 1, N);
-            a.first_wg[bg] = (int32_t)w0;
-            segs += (int)(w1 - w0 + 1);
+            const uint32_t u0 = (uint32_t)tp[b] * a.Hkv + g * nb;
+            const int w0 = (int)split.owner(u0), w1 = (int)split.owner(u0 + nb - 1);
+            a.first_wg[bg] = w0;
+            segs += w1 - w0 + 1;
         }
     }
     int nseg;
     run = block_excl_scan<NT>(segs, scan_lds, &nseg);
     for (int bg = g0; bg < g1; ++bg) {
         const int b = bg / a.Hkv, g = bg - b * a.Hkv;
-        const int64_t nb = tp[b + 1] - tp[b];
+        const int nb = tp[b + 1] - tp[b];
         if (nb) {
-            const int64_t u0 = (int64_t)tp[b] * a.Hkv + g * nb;
-            run += (int)(div_floor((u0 + nb) * We - 1, N) - div_floor((u0 + 1) * We - 1, N) + 1);
+            const uint32_t u0 = (uint32_t)tp[b] * a.Hkv + g * nb;
+            run += (int)(split.owner(u0 + nb - 1) - split.owner(u0) + 1);
         }
         a.seg_prefix[bg + 1] = run;
     }
@@ -93,7 +98,7 @@ __device__ void plan_partition(const PlanArgs &a, const int32_t *tp, int n, int 
     int sb = 0;
     if (w0 < w1 && We > 0) {
         // largest item i in [0, n) with Hkv * tp[i] <= begin(w0)
-        const int64_t begin = w0 <= We ? div_floor((int64_t)w0 * N, We) : N;
+        const int64_t begin = w0 <= We ? split.begin(w0) : N;
         int lo = 0, hi = n - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
@@ -105,7 +110,7 @@ __device__ void plan_partition(const PlanArgs &a, const int32_t *tp, int n, int 
         sb = lo;
     }
     for (int w = w0; w < w1; ++w) {
-        const int64_t begin = (w <= We && We > 0) ? div_floor((int64_t)w * N, We) : N;
+        const int64_t begin = (w <= We && We > 0) ? split.begin(w) : N;
         a.wg_begin[w] = (int32_t)begin;
         if (w < a.W) {
             if (w < We) {
@@ -230,7 +235,8 @@ __global__ __launch_bounds__(kST) void plan_shared_kernel(PlanArgs a)
     __shared__ int32_t share_lds[kMaxBatch];    // tokens shared with the previous request
     __shared__ int32_t len_lds[kMaxBatch];      // validated lengths
     __shared__ int scan_lds[kSW];
-    __shared__ int red_lds[2 * kSW];
+    __shared__ int run_lds[3 * kSW];   // (each block pass has its own LDS, so one barrier each)
+    __shared__ int cnt_lds[2 * kSW];
     const int tid = threadIdx.x;
     const int R = shared_group(a.G);
     const int64_t limit = (int64_t)a.pt_stride * a.P;
@@ -240,126 +246,114 @@ __global__ __launch_bounds__(kST) void plan_shared_kernel(PlanArgs a)
     // 1) tokens shared with the previous request: leading page slots with the
     //    same valid id, capped by both lengths, whole tiles; and the validated
     //    lengths (out-of-range lengths count as 0 and set the status bit). It
-    //    reads only the inputs, so it goes first. Lane l of a wave
-    //    compares slots 4l..4l+3 (256 consecutive slots per step, coalesced);
-    //    a ballot over the lanes whose 4 slots all agree finds the first
-    //    mismatch. Each of the 16 waves takes kNB requests at a time
-    //    (b = wave + 16 k), so all their loads share one round trip per step,
-    //    and the first step's loads go out together with the lengths';
-    //    the round trips, not the bytes, are what this phase costs (a wave
-    //    holds at most 63 loads in flight, hence the 16 waves).
+    //    reads only the inputs, so it goes first. Each wave takes kNB
+    //    consecutive requests at a time and loads the kNB + 1 page-table rows
+    //    they span once (row b is request b's row and request b + 1's
+    //    previous one), 256 slots each: lane l holds slots l + 64 i, so every
+    //    load instruction reads contiguous bytes. The lengths come in one load
+    //    issued first, and one wait covers the step. The per-request
+    //    arithmetic runs across lanes (lane k: request base + k); only the
+    //    search for the first slot that differs, one ballot per 64 slots, runs
+    //    per request. A run that goes on past 256 slots continues in further
+    //    steps for its request alone.
     int mx = 0, st = 0;
     {
-        constexpr int kNB = 8, kSub = 4, kSpan = 64 * kSub;
-        const int wave = tid >> 6, lane = tid & 63;
-        for (int base = wave; base < a.B; base += kSW * kNB) {
-            int c[kNB], n[kNB], lmin[kNB];
-            bool done[kNB];
-            int x[kNB][kSub], y[kNB][kSub];
-            // the first step's slots of rows b and b - 1 do not depend on the
-            // lengths: their loads go out with the lengths' (one round trip)
+        constexpr int kNB = 64 / kSW, kSub = 4, kSpan = 64 * kSub;
+        // (wave-uniform in scalar registers: rows and their addresses are scalar)
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+        // first slot in [c0, c0 + kSpan) where xs and ys differ (or either is
+        // not a valid page id, or the slot is at or past nk); kSpan if none
+        auto first_mismatch = [&](const int (&xs)[kSub], const int (&ys)[kSub], int c0, int nk) {
+            int run = kSpan;
+#pragma unroll
+            for (int i = kSub - 1; i >= 0; --i) {
+                const bool ok = c0 + lane + 64 * i < nk && xs[i] == ys[i] && xs[i] >= 0 && xs[i] < a.num_pages;
+                const uint64_t full = __builtin_amdgcn_ballot_w64(ok);
+                if (full != ~0ull)
+                    run = 64 * i + __builtin_ctzll(~full);
+            }
+            return run;
+        };
+        auto load_row = [&](int (&xs)[kSub], int row, int c0, int nk) {
+            const int32_t *ra = a.page_table + (size_t)row * a.pt_stride;
+#pragma unroll
+            for (int i = 0; i < kSub; ++i) {
+                const int j = c0 + lane + 64 * i;
+                xs[i] = j < nk ? ra[j] : -1;
+            }
+        };
+        for (int base = wave * kNB; base < a.B; base += kSW * kNB) {
+            // lane r <= kNB: the length of row base - 1 + r
+            const int lv = a.lengths[max(min(base - 1 + lane, a.B - 1), 0)];
+            // rows base - 1 .. base + kNB - 1, slots lane + 64 i (-1 past the
+            // row's end or for a row outside [0, B))
+            int rw[kNB + 1][kSub];
+#pragma unroll
+            for (int i = 0; i < kSub; ++i) {
+#pragma unroll
+                for (int r = 0; r <= kNB; ++r)
+                    rw[r][i] = -1;
+                if (lane + 64 * i < a.pt_stride) {
+#pragma unroll
+                    for (int r = 0; r <= kNB; ++r) {
+                        const int row = base - 1 + r;
+                        if (row >= 0 && row < a.B)
+                            rw[r][i] = a.page_table[(size_t)row * a.pt_stride + lane + 64 * i];
+                    }
+                }
+            }
+            // lane k < kNB: request b = base + k, its length and the previous request's
+            const int b = base + lane;
+            const bool mine = lane < kNB && b < a.B;
+            int la = __shfl_down(lv, 1), lp = lv;
+            if (mine && (la < 0 || (int64_t)la > limit))
+                st = 1;
+            la = (la < 0 || (int64_t)la > limit) ? 0 : la;
+            lp = (lp < 0 || (int64_t)lp > limit) ? 0 : lp;
+            if (mine) {
+                mx = max(mx, la);
+                len_lds[b] = la;
+            }
+            const int lmin = min(la, lp);
+            const int nv = mine && b > 0 ? (lmin + a.P - 1) / a.P : 0;   // slots to compare
+            int cv = 0;   // lane k: the common run of request k, in slots
 #pragma unroll
             for (int k = 0; k < kNB; ++k) {
-                const int b = base + kSW * k;
-                const int32_t *ra = a.page_table + (size_t)b * a.pt_stride;
-#pragma unroll
-                for (int i = 0; i < kSub; ++i) {
-                    const int j = kSub * lane + i;
-                    x[k][i] = -1;
-                    y[k][i] = -2;
-                    if (b > 0 && b < a.B && j < a.pt_stride) {
-                        x[k][i] = ra[j];
-                        y[k][i] = ra[j - a.pt_stride];
-                    }
+                const int nk = __builtin_amdgcn_readlane(nv, k);
+                if (nk == 0)
+                    continue;
+                int c = first_mismatch(rw[k + 1], rw[k], 0, nk);
+                // further steps while a whole 256-slot window agreed (each
+                // adds 256 to c < nk, so the loop ends)
+                bool more = c == kSpan && c < nk;
+                while (more) {
+                    int x[kSub], y[kSub];
+                    load_row(x, base + k, c, nk);
+                    load_row(y, base + k - 1, c, nk);
+                    const int run = first_mismatch(x, y, c, nk);
+                    c += run;
+                    more = run == kSpan && c < nk;
                 }
+                cv = lane == k ? c : cv;
             }
-#pragma unroll
-            for (int k = 0; k < kNB; ++k) {
-                // branch-free, in-bounds loads
-                const int b = base + kSW * k;
-                const int ia = max(min(b, a.B - 1), 0), ip = max(ia - 1, 0);
-                int la = a.lengths[ia], lp = a.lengths[ip];
-                if (b < a.B && (la < 0 || (int64_t)la > limit))
-                    st = 1;
-                la = (la < 0 || (int64_t)la > limit) ? 0 : la;
-                lp = (lp < 0 || (int64_t)lp > limit) ? 0 : lp;
-                if (b < a.B) {
-                    mx = max(mx, la);
-                    if (lane == 0)
-                        len_lds[b] = la;
-                }
-                lmin[k] = min(la, lp);
-                c[k] = 0;
-                n[k] = (b > 0 && b < a.B) ? (lmin[k] + a.P - 1) / a.P : 0;
-                done[k] = n[k] == 0;
-            }
-            for (bool first = true;; first = false) {
-                if (!first) {
-#pragma unroll
-                    for (int k = 0; k < kNB; ++k) {
-                        const int32_t *ra = a.page_table + (size_t)(base + kSW * k) * a.pt_stride;
-#pragma unroll
-                        for (int i = 0; i < kSub; ++i) {
-                            x[k][i] = -1;
-                            y[k][i] = -2;
-                            const int j = c[k] + kSub * lane + i;
-                            if (!done[k] && j < n[k]) {
-                                x[k][i] = ra[j];
-                                y[k][i] = ra[j - a.pt_stride];
-                            }
-                        }
-                    }
-                }
-                bool any = false;
-#pragma unroll
-                for (int k = 0; k < kNB; ++k) {
-                    if (done[k])
-                        continue;
-                    int m = 0;   // this lane's slots that agree (slots past n do not)
-#pragma unroll
-                    for (int i = 0; i < kSub; ++i)
-                        m |= (c[k] + kSub * lane + i < n[k] && x[k][i] == y[k][i] && x[k][i] >= 0 &&
-                              x[k][i] < a.num_pages)
-                             << i;
-                    const uint64_t full = __builtin_amdgcn_ballot_w64(m == (1 << kSub) - 1);
-                    int run = kSpan;
-                    if (full != ~0ull) {
-                        const int fl = __builtin_ctzll(~full);   // first lane with a mismatch
-                        const int mf = __builtin_amdgcn_readlane(m, fl);
-                        run = kSub * fl + __builtin_ctz(~mf);
-                    }
-                    c[k] += run;
-                    done[k] = run < kSpan || c[k] >= n[k];
-                    any |= !done[k];
-                }
-                if (!any)
-                    break;
-            }
-            if (lane == 0) {
-#pragma unroll
-                for (int k = 0; k < kNB; ++k) {
-                    const int b = base + kSW * k;
-                    if (b < a.B) {
-                        const int64_t t = b > 0 ? min((int64_t)c[k] * a.P, (int64_t)lmin[k]) : 0;
-                        share_lds[b] = (int)(t / a.T * a.T);
-                    }
-                }
+            if (mine) {
+                const int64_t t = b > 0 ? min((int64_t)cv * a.P, (int64_t)lmin) : 0;
+                share_lds[b] = (int)(t / a.T * a.T);
             }
         }
     }
 
-    // 2) the largest length and the status bit (the barriers of the reduction
-    //    also publish share_lds and len_lds)
-    int maxle, status;
-    block_max_or<kST>(mx, st, red_lds, &maxle, &status);
+    __syncthreads();   // share_lds and len_lds are complete
 
-    // 3) runs (start at b = 0 and wherever share = 0), groups of R, and the
-    //    item and tile counts of each thread's requests
+    // 2) runs (start at b = 0 and wherever share = 0), groups of R, and the
+    //    item and tile counts of each thread's requests; the largest length
+    //    and the status bit reduce in the same pass as the runs' starts
     int last_start = -1;
     for (int b = b0; b < b1; ++b)
         if (b == 0 || share_lds[b] == 0)
             last_start = b;
-    const int carry = block_excl_max_scan<kST>(last_start, -1, scan_lds);
+    int maxle, status;
+    const int carry = block_excl_max_scan_max_or<kST>(last_start, -1, mx, st, run_lds, &maxle, &status);
     int nitems = 0, ntiles = 0;
     {
         int rs = carry;
@@ -376,11 +370,10 @@ __global__ __launch_bounds__(kST) void plan_shared_kernel(PlanArgs a)
             ntiles += (len_lds[b] - Ls + a.T - 1) / a.T;
         }
     }
-    int n_items, total;
-    const int ibase = block_excl_scan<kST>(nitems, scan_lds, &n_items);
-    const int tbase = block_excl_scan<kST>(ntiles, scan_lds, &total);
+    int n_items, total, ibase, tbase;
+    block_excl_scan2<kST>(nitems, ntiles, cnt_lds, &ibase, &tbase, &n_items, &total);
 
-    // 4) items, in request order
+    // 3) items, in request order
     {
         int i = ibase, t = tbase, rs = carry;
         for (int b = b0; b < b1; ++b) {
@@ -423,9 +416,13 @@ __global__ __launch_bounds__(kST) void plan_shared_kernel(PlanArgs a)
     }
     __syncthreads();
 
-    // 5) the dynamic partition over items (tiles prefix from LDS when it fits)
-    plan_partition<kST>(a, n_items <= kMaxBatch ? tp_lds : a.tiles_prefix, n_items, total, status, maxle, n_items, R,
-                   scan_lds);
+    // 4) the dynamic partition over items (tiles prefix from LDS when it fits;
+    //    two calls, so that each reads its array with its own instructions
+    //    rather than generic ones)
+    if (n_items <= kMaxBatch)
+        plan_partition<kST>(a, tp_lds, n_items, total, status, maxle, n_items, R, scan_lds);
+    else
+        plan_partition<kST>(a, a.tiles_prefix, n_items, total, status, maxle, n_items, R, scan_lds);
 }
 
 }  // namespace

@@ -146,29 +146,71 @@ __device__ __forceinline__ int block_excl_max_scan(int v, int lo, int *lds)
     return excl;
 }
 
-// Max and OR of one int per thread over a workgroup of NT threads; `lds` holds
-// 2*NT/64 ints.
+// Exclusive running maximum of one int per thread (as block_excl_max_scan),
+// with the workgroup's maximum of a second int and OR of a third, through a
+// single barrier. `lds` holds 3*NT/64 ints and must not be written again
+// before the caller's next barrier. Every thread of the workgroup must call it.
 template <int NT>
-__device__ __forceinline__ void block_max_or(int mx, int bits, int *lds, int *mx_out, int *bits_out)
+__device__ __forceinline__ int block_excl_max_scan_max_or(int v, int lo, int mx, int bits, int *lds, int *mx_out,
+                                                          int *bits_out)
 {
     constexpr int NW = NT / 64;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int incl = wave_incl_scan_op(v, INT_MIN, OpMax{});
+    int excl = __shfl_up(incl, 1, 64);
+    if (lane == 0)
+        excl = lo;
     mx = wave_max(mx);
     bits = wave_or(bits);
+    if (lane == 63)
+        lds[wave] = incl;
     if (lane == 0) {
-        lds[wave] = mx;
-        lds[NW + wave] = bits;
+        lds[NW + wave] = mx;
+        lds[2 * NW + wave] = bits;
     }
     __syncthreads();
-    int m = 0, o = 0;
+    int m = INT_MIN, o = 0;
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
-        m = max(m, lds[i]);
-        o |= lds[NW + i];
+        if (i < wave)
+            excl = max(excl, lds[i]);
+        m = max(m, lds[NW + i]);
+        o |= lds[2 * NW + i];
     }
-    __syncthreads();
     *mx_out = m;
     *bits_out = o;
+    return excl;
+}
+
+// Exclusive prefix sums of two ints per thread over a workgroup of NT threads
+// (in thread order), through a single barrier; *total1 / *total2 receive the
+// sums. `lds` holds 2*NT/64 ints and must not be written again before the
+// caller's next barrier. Every thread of the workgroup must call it.
+template <int NT>
+__device__ __forceinline__ void block_excl_scan2(int v1, int v2, int *lds, int *excl1, int *excl2, int *total1,
+                                                 int *total2)
+{
+    constexpr int NW = NT / 64;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int i1 = wave_incl_scan(v1), i2 = wave_incl_scan(v2);
+    if (lane == 63) {
+        lds[wave] = i1;
+        lds[NW + wave] = i2;
+    }
+    __syncthreads();
+    int b1 = 0, b2 = 0, a1 = 0, a2 = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const int t1 = lds[i], t2 = lds[NW + i];
+        b1 += i < wave ? t1 : 0;
+        b2 += i < wave ? t2 : 0;
+        a1 += t1;
+        a2 += t2;
+    }
+    *excl1 = b1 + i1 - v1;
+    *excl2 = b2 + i2 - v2;
+    *total1 = a1;
+    *total2 = a2;
 }
 
 // The uniform partition of N units into We contiguous ranges, range w being
@@ -199,17 +241,6 @@ struct UniformSplit {
         return (uint32_t)w;
     }
 };
-
-// floor(x / d) for 0 <= x < 2^53, d > 0: double estimate, exact correction.
-__device__ __forceinline__ int64_t div_floor(int64_t x, int64_t d)
-{
-    int64_t q = (int64_t)((double)x / (double)d);
-    if (q * d > x)
-        --q;
-    else if ((q + 1) * d <= x)
-        ++q;
-    return q;
-}
 
 __device__ __forceinline__ int64_t gcd64(int64_t a, int64_t b)
 {
