@@ -53,39 +53,34 @@ __device__ void plan_partition(const PlanArgs &a, const int32_t *tp, int n, int 
 {
     const int tid = threadIdx.x;
     int run;
-    // segments per (item, g) and their prefix. The owner of unit u,
-    // floor(((u + 1) We - 1) / N), is the largest w with begin(w) <= u: the
-    // 32-bit uniform split computes both (N < 2^31 and We <= 2^16 by the
-    // shape checks).
+    // segments per (item, g) and their prefix
     const int nbg = n * a.Hkv;
     const int64_t N = (int64_t)total * a.Hkv;
     const int64_t We = plan_wgs(N, a.W, a.W_auto);
-    UniformSplit split;
-    if (We > 0)
-        split.init((uint32_t)N, (uint32_t)We);
     const int cB = (nbg + NT - 1) / NT;
     const int g0 = min(nbg, tid * cB), g1 = min(nbg, g0 + cB);
     int segs = 0;
     for (int bg = g0; bg < g1; ++bg) {
         const int b = bg / a.Hkv, g = bg - b * a.Hkv;
-        const int nb = tp[b + 1] - tp[b];
+        const int64_t nb = tp[b + 1] - tp[b];
         if (nb == 0) {
             a.first_wg[bg] = -1;
         } else {
-            const uint32_t u0 = (uint32_t)tp[b] * a.Hkv + g * nb;
-            const int w0 = (int)split.owner(u0), w1 = (int)split.owner(u0 + nb - 1);
-            a.first_wg[bg] = w0;
-            segs += w1 - w0 + 1;
+            const int64_t u0 = (int64_t)tp[b] * a.Hkv + g * nb;
+            const int64_t w0 = div_floor((u0 + 1) * We - 1, N);
+            const int64_t w1 = div_floor((u0 + nb) * We - 1, N);
+            a.first_wg[bg] = (int32_t)w0;
+            segs += (int)(w1 - w0 + 1);
         }
     }
     int nseg;
     run = block_excl_scan<NT>(segs, scan_lds, &nseg);
     for (int bg = g0; bg < g1; ++bg) {
         const int b = bg / a.Hkv, g = bg - b * a.Hkv;
-        const int nb = tp[b + 1] - tp[b];
+        const int64_t nb = tp[b + 1] - tp[b];
         if (nb) {
-            const uint32_t u0 = (uint32_t)tp[b] * a.Hkv + g * nb;
-            run += (int)(split.owner(u0 + nb - 1) - split.owner(u0) + 1);
+            const int64_t u0 = (int64_t)tp[b] * a.Hkv + g * nb;
+            run += (int)(div_floor((u0 + nb) * We - 1, N) - div_floor((u0 + 1) * We - 1, N) + 1);
         }
         a.seg_prefix[bg + 1] = run;
     }
@@ -98,7 +93,7 @@ __device__ void plan_partition(const PlanArgs &a, const int32_t *tp, int n, int 
     int sb = 0;
     if (w0 < w1 && We > 0) {
         // largest item i in [0, n) with Hkv * tp[i] <= begin(w0)
-        const int64_t begin = w0 <= We ? split.begin(w0) : N;
+        const int64_t begin = w0 <= We ? div_floor((int64_t)w0 * N, We) : N;
         int lo = 0, hi = n - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
@@ -110,7 +105,7 @@ __device__ void plan_partition(const PlanArgs &a, const int32_t *tp, int n, int 
         sb = lo;
     }
     for (int w = w0; w < w1; ++w) {
-        const int64_t begin = (w <= We && We > 0) ? split.begin(w) : N;
+        const int64_t begin = (w <= We && We > 0) ? div_floor((int64_t)w * N, We) : N;
         a.wg_begin[w] = (int32_t)begin;
         if (w < a.W) {
             if (w < We) {

@@ -242,6 +242,17 @@ struct UniformSplit {
     }
 };
 
+// floor(x / d) for 0 <= x < 2^53, d > 0: double estimate, exact correction.
+__device__ __forceinline__ int64_t div_floor(int64_t x, int64_t d)
+{
+    int64_t q = (int64_t)((double)x / (double)d);
+    if (q * d > x)
+        --q;
+    else if ((q + 1) * d <= x)
+        ++q;
+    return q;
+}
+
 __device__ __forceinline__ int64_t gcd64(int64_t a, int64_t b)
 {
     while (b) {
