@@ -26,12 +26,12 @@ reported baseline) also checks each of them against the oracle ("parity"),
 and the process exits with status 1 if any is out of bounds.
 
 Prints ONE JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-Profile summaries: --kernel-stats DIR OUT_JSON, --traffic-summary FETCH_DIR
-WRITE_DIR PROBE_OUTPUT OUT_JSON (rocprofv3 output directories, see profiles/).
+Profile summaries: --kernel-stats DIR OUT_JSON [BENCH_OUTPUT], --traffic-summary
+FETCH_DIR WRITE_DIR PROBE_OUTPUT OUT_JSON (rocprofv3 output directories, see
+profiles/).
 """
 import argparse
 import hashlib
-import re
 import json
 import math
 import os
@@ -59,26 +59,26 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-_CODE_TOKENS = re.compile(r'"(?:\\.|[^"\\\n])*"'      # string literal
-                          r"|'(?:\\.|[^'\\\n])*'"       # character literal
-                          r"|//[^\n]*"                       # line comment
-                          r"|/\*.*?\*/"                     # block comment
-                          r"|\S+?(?=//|/\*|[\s\"']|$)"     # any other run of code
-                          r"|\S", re.S)
-
-
-def source_hash():
-    """Hash of the decode kernels' code, blind to comments and to the width of
-    whitespace, so a profile taken before a comment-only edit still matches
-    the kernel."""
-    h = hashlib.sha256()
-    for f in ("decode.hip", "vlkv_internal.hpp", "vlkv_device.hpp"):
-        with open(os.path.join(ROOT, "variable_length_kv_amd", "csrc", f), encoding="utf-8") as fh:
-            text = fh.read()
-        for tok in _CODE_TOKENS.findall(text):
-            if not tok.startswith(("//", "/*")):
-                h.update(tok.encode() + b"\0")
-    return h.hexdigest()[:16]
+def code_hash():
+    """Hash of the device code inside the built library (its .hip_fatbin
+    section, every kernel of it): a committed profile counts for the kernels
+    only while the library carries the code it was taken on. Comments and
+    host-side edits leave it unchanged; the section records the build
+    directory too, so it is compared on the tree that built it."""
+    import struct
+    path = os.path.join(ROOT, "variable_length_kv_amd", "libvlkv_attn.so")
+    if not os.path.exists(path):
+        return None
+    with open(path, "rb") as f:
+        b = f.read()
+    shoff = struct.unpack_from("<Q", b, 0x28)[0]
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", b, 0x3A)
+    secs = [struct.unpack_from("<IIQQQQ", b, shoff + i * shentsize) for i in range(shnum)]
+    names = secs[shstrndx][4]
+    for name, _typ, _flags, _addr, off, size in secs:
+        if b[names + name:b.index(b"\0", names + name)] == b".hip_fatbin":
+            return hashlib.sha256(b[off:off + size]).hexdigest()[:16]
+    return None
 
 
 def us(x_ms):
@@ -663,7 +663,7 @@ def traffic_probe(torch, L, W, reps=3):
         r8.step(att8, True)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": src.numel() * 4, "decode_kv_bytes": c1.kv_bytes,
-                      "decode_kv_bytes_fp8": c8.kv_bytes, "reps": reps, "source_hash": source_hash()}), flush=True)
+                      "decode_kv_bytes_fp8": c8.kv_bytes, "reps": reps, "code_hash": code_hash()}), flush=True)
 
 
 def router_probe(torch, L, reps=3):
@@ -695,12 +695,12 @@ def router_probe(torch, L, reps=3):
 
 def traffic_entry(kernel):
     """HBM bytes per launch of `kernel` from committed rocprofv3 counters, only
-    if they were taken on the current kernel source."""
+    if they were taken on the library's current device code."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as f:
         t = json.load(f)
-    if t.get("source_hash") != source_hash():
+    if t.get("code_hash") is None or t.get("code_hash") != code_hash():
         return None
     k = t.get("kernels", {}).get(kernel)
     return None if k is None else k.get("hbm_bytes_per_launch")
@@ -708,12 +708,12 @@ def traffic_entry(kernel):
 
 def kernel_stats_entry(kernel):
     """Average duration (ns) of `kernel` in the committed rocprofv3 kernel
-    trace of the headline command, only if taken on the current kernel source."""
+    trace of the headline command, only if taken on the library's current device code."""
     if not os.path.exists(KERNEL_STATS_FILE):
         return None
     with open(KERNEL_STATS_FILE) as f:
         t = json.load(f)
-    if t.get("source_hash") != source_hash():
+    if t.get("code_hash") is None or t.get("code_hash") != code_hash():
         return None
     k = t.get("kernels", {}).get(kernel)
     return None if k is None else k.get("avg_ns")
@@ -726,9 +726,17 @@ def _short_name(name):
     return n.split("::")[-1].strip()
 
 
-def write_kernel_stats(d, out_json):
+def write_kernel_stats(d, out_json, bench_output=None):
+    """Summarise a rocprofv3 kernel trace. ``bench_output``: the profiled
+    bench run's output, whose JSON line names the device code it ran (else the
+    library here is taken to be that code)."""
     import csv
     import glob
+    h = code_hash()
+    if bench_output:
+        with open(bench_output) as f:
+            line = [l for l in f.read().splitlines() if l.startswith("{")][-1]
+        h = json.loads(line)["roofline"]["code_hash"]
     files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
     if not files:
         raise SystemExit(f"no kernel_stats.csv under {d}")
@@ -736,7 +744,7 @@ def write_kernel_stats(d, out_json):
     for row in csv.DictReader(open(files[0])):
         kernels[_short_name(row["Name"])] = {"calls": int(row["Calls"]), "avg_ns": float(row["AverageNs"]),
                                              "min_ns": float(row["MinNs"]), "max_ns": float(row["MaxNs"])}
-    res = {"source_hash": source_hash(), "stats_file": os.path.basename(files[0]), "kernels": kernels}
+    res = {"code_hash": h, "stats_file": os.path.basename(files[0]), "kernels": kernels}
     with open(out_json, "w") as f:
         json.dump(res, f, indent=1)
     print(json.dumps(res, indent=1))
@@ -783,7 +791,7 @@ def write_traffic_summary(fetch_dir, write_dir, probe_output, out_json):
     fs, ws = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
     alg = probe["decode_kv_bytes"]
     res = {"workload": "uniform-mixed, 32 requests, 284965 tokens (headline step)",
-           "source_hash": probe["source_hash"], "copy_fetch_kib": round(cf, 1), "copy_write_kib": round(cw, 1),
+           "code_hash": probe["code_hash"], "copy_fetch_kib": round(cf, 1), "copy_write_kib": round(cw, 1),
            "fetch_scale": round(fs, 5), "write_scale": round(ws, 5), "algorithmic_bytes_per_launch": alg,
            "kernels": {}}
     for k in (FUSED_KERNEL, THREE_KERNEL, "plan_kernel", "combine_kernel"):
@@ -817,12 +825,15 @@ def main():
                     help="only the launches that the rocprofv3 --pmc runs measure")
     ap.add_argument("--router-probe", action="store_true",
                     help="only the router GEMM launches that its rocprofv3 runs measure")
-    ap.add_argument("--kernel-stats", nargs=2, metavar=("ROCPROF_DIR", "OUT_JSON"),
-                    help="summarise a rocprofv3 --kernel-trace --stats run (no GPU work)")
+    ap.add_argument("--kernel-stats", nargs="+", metavar="ARG",
+                    help="ROCPROF_DIR OUT_JSON [BENCH_OUTPUT]: summarise a rocprofv3 --kernel-trace --stats "
+                         "run of this bench (no GPU work)")
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "PROBE_OUTPUT", "OUT_JSON"),
                     help="summarise the FETCH_SIZE and WRITE_SIZE rocprofv3 --pmc runs of --traffic-probe")
     args = ap.parse_args()
     if args.kernel_stats:
+        if len(args.kernel_stats) not in (2, 3):
+            ap.error("--kernel-stats takes ROCPROF_DIR OUT_JSON [BENCH_OUTPUT]")
         write_kernel_stats(*args.kernel_stats)
         return
     if args.traffic_summary:
@@ -911,6 +922,7 @@ def main():
                      "algorithmic_bytes_per_launch": kv, "launch_avg_us": us(launch_ms),
                      "launch_timing": "HIP events around each launch on the library's stream, after a 1 GiB "
                                       "sweep (dispatch included)",
+                     "code_hash": code_hash(),
                      "rocprof": None if rp is None else {
                          "avg_us": round(rp / 1e3, 2),
                          "frac": round(kv / (rp * 1e-9) / 1e9 / HBM_PEAK_GBS, 4),

@@ -44,11 +44,11 @@ def test_settle_runs_both_forms_and_stops():
     assert run.fused_calls == run.three_calls == n
 
 
-def test_traffic_counters_follow_the_kernel_source():
+def test_traffic_counters_follow_the_device_code():
     with open(bench.TRAFFIC_FILE) as f:
         t = json.load(f)
     entry = bench.traffic_entry(bench.FUSED_KERNEL)
-    if t["source_hash"] == bench.source_hash():
+    if t["code_hash"] == bench.code_hash():
         assert entry == t["kernels"][bench.FUSED_KERNEL]["hbm_bytes_per_launch"]
         # every K/V byte fetched once, plus a little (q, page table, partials)
         assert 1.0 <= t["kernels"][bench.FUSED_KERNEL]["read_over_algorithmic"] < 1.05
@@ -81,6 +81,40 @@ def test_compare_flags_out_of_bound_outputs():
     assert not bench.compare(out, lfin, ref, ref_l, "bf16")["ok"]
 
 
+def test_code_hash_reads_the_device_code_section(tmp_path, monkeypatch):
+    """The hash covers the library's .hip_fatbin section and nothing else: a
+    minimal ELF with that section hashes its bytes; changing another section
+    leaves the hash alone, changing the section changes it."""
+    import hashlib
+    import struct
+
+    def elf(fatbin, other):
+        names = b"\0.shstrtab\0.hip_fatbin\0.text\0"
+        data = names + fatbin + other
+        shoff = 64 + len(data)
+        secs = [(0, 0, 0, 0, 0, 0),
+                (1, 3, 0, 0, 64, len(names)),                                  # .shstrtab
+                (11, 1, 2, 0, 64 + len(names), len(fatbin)),                   # .hip_fatbin
+                (23, 1, 6, 0, 64 + len(names) + len(fatbin), len(other))]      # .text
+        head = bytearray(64)
+        head[:4] = b"\x7fELF"
+        struct.pack_into("<Q", head, 0x28, shoff)
+        struct.pack_into("<HHH", head, 0x3A, 64, len(secs), 1)
+        body = b"".join(struct.pack("<IIQQQQ", *sec) + bytes(24) for sec in secs)
+        return bytes(head) + data + body
+
+    lib_dir = tmp_path / "variable_length_kv_amd"
+    lib_dir.mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (lib_dir / "libvlkv_attn.so").write_bytes(elf(b"DEVICE-CODE-1", b"host code A"))
+    h1 = bench.code_hash()
+    assert h1 == hashlib.sha256(b"DEVICE-CODE-1").hexdigest()[:16]
+    (lib_dir / "libvlkv_attn.so").write_bytes(elf(b"DEVICE-CODE-1", b"host code B, longer"))
+    assert bench.code_hash() == h1
+    (lib_dir / "libvlkv_attn.so").write_bytes(elf(b"DEVICE-CODE-2", b"host code A"))
+    assert bench.code_hash() != h1
+
+
 def test_profile_kernel_names():
     assert bench._short_name("vlkv::(anonymous namespace)::decode_kernel<2, 0>(vlkv::DecodeArgs)") == \
         "decode_kernel<2, 0>"
@@ -88,13 +122,13 @@ def test_profile_kernel_names():
     assert bench._short_name("__amd_rocclr_copyBuffer") == "__amd_rocclr_copyBuffer"
 
 
-def test_kernel_stats_follow_the_kernel_source():
+def test_kernel_stats_follow_the_device_code():
     if not os.path.exists(bench.KERNEL_STATS_FILE):
         return
     with open(bench.KERNEL_STATS_FILE) as f:
         t = json.load(f)
     avg = bench.kernel_stats_entry(bench.FUSED_KERNEL)
-    if t["source_hash"] == bench.source_hash():
+    if t["code_hash"] == bench.code_hash():
         assert avg == t["kernels"][bench.FUSED_KERNEL]["avg_ns"]
     else:
         assert avg is None

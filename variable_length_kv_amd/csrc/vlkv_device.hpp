@@ -124,31 +124,9 @@ __device__ __forceinline__ int block_scan_max_or(int v, int mx, int bits, int *l
 }
 
 // Exclusive running maximum of one int per thread over a workgroup of NT
-// threads (in thread order); `lo` is the identity (returned to thread 0).
-// `lds` holds NT/64 ints. Every thread of the workgroup must call it.
-template <int NT>
-__device__ __forceinline__ int block_excl_max_scan(int v, int lo, int *lds)
-{
-    constexpr int NW = NT / 64;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int incl = wave_incl_scan_op(v, INT_MIN, OpMax{});
-    int excl = __shfl_up(incl, 1, 64);
-    if (lane == 0)
-        excl = lo;
-    if (lane == 63)
-        lds[wave] = incl;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < NW; ++i)
-        if (i < wave)
-            excl = max(excl, lds[i]);
-    __syncthreads();  // lds is reused by the next call
-    return excl;
-}
-
-// Exclusive running maximum of one int per thread (as block_excl_max_scan),
-// with the workgroup's maximum of a second int and OR of a third, through a
-// single barrier. `lds` holds 3*NT/64 ints and must not be written again
+// threads (in thread order; `lo` is the identity, returned to thread 0), with
+// the workgroup's maximum of a second int and OR of a third, through a single
+// barrier. `lds` holds 3*NT/64 ints and must not be written again
 // before the caller's next barrier. Every thread of the workgroup must call it.
 template <int NT>
 __device__ __forceinline__ int block_excl_max_scan_max_or(int v, int lo, int mx, int bits, int *lds, int *mx_out,
