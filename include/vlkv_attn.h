@@ -67,9 +67,12 @@ extern "C" {
 /* status word bits (attn_get_status) */
 #define ATTN_STATUS_BAD_LENGTH  1u  /* some L_b < 0 or L_b > pt_stride * page_size: treated as 0 */
 #define ATTN_STATUS_BAD_PAGE    2u  /* some used page id outside [0, num_pages): its rows skipped */
-#define ATTN_STATUS_INTERNAL    4u  /* attn_step: a workgroup's range split more than its first and
-                                       last (request, kv head) pair, which the plan rules out; the
-                                       extra pair was not merged (a library defect, never data) */
+#define ATTN_STATUS_INTERNAL    4u  /* a library defect, never data: in attn_step a workgroup's range
+                                       split more than its first and last (request, kv head) pair,
+                                       which the plan rules out (the extra pair was not merged); or,
+                                       in any decode, a wait of the waves of one workgroup for one
+                                       another at a segment's end ran out its bound (that segment's
+                                       merge was skipped). Either way some outputs are wrong. */
 
 /*
  * Problem shape (host struct, read during the call).
