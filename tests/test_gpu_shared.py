@@ -64,13 +64,36 @@ def test_device_plan_matches_spec(seed):
 
 def test_device_plan_long_prefixes_and_large_batch():
     """Many requests, prefixes of hundreds of pages: the page-slot comparison
-    runs over many 16-slot steps."""
+    runs over several 256-slot steps."""
     lengths, groups = wl.shared_prefix_lengths(40, 5, 24576, 1, 3000, 64, seed=3)
     pt, num_pages = wl.shared_page_table(lengths, groups, 64, 7)
     for G in (1, 4, 8, 16):
         got = _device_plan(lengths, pt, 8, G, 64, num_pages, 64, 512)
         ref = oracle.plan_shared(lengths, pt, 8, G, 64, num_pages, 64, 512)
         _compare_plan(got, ref)
+
+
+@pytest.mark.parametrize("run", [255, 256, 257, 511, 512, 513])
+def test_device_plan_shared_runs_at_step_boundaries(run):
+    """Common runs of page ids that end just before, at and just after the
+    planner's 256-slot comparison steps (one and two steps), for a group of
+    four requests after a request that shares nothing, one member ending a
+    page inside the run."""
+    P, stride = 16, 600
+    rng = np.random.default_rng(run)
+    num_pages = 5 * stride + 10
+    perm = rng.permutation(num_pages).astype(np.int32)
+    pt = perm[:5 * stride].reshape(5, stride).copy()
+    for b in (2, 3, 4):
+        pt[b, :run] = pt[1, :run]                   # requests 1-4 share their first `run` pages
+    # (request 2 runs past the shared pages, so its comparison with request 1
+    # goes on into a further step whose first slot already differs)
+    lengths = np.array([stride * P, stride * P, stride * P, (run - 1) * P + 3, stride * P], np.int64)
+    for G in (1, 8):
+        for W in (1, 37):
+            got = _device_plan(lengths, pt, 2, G, P, num_pages, 64, W)
+            ref = oracle.plan_shared(lengths, pt, 2, G, P, num_pages, 64, W)
+            _compare_plan(got, ref)
 
 
 def _shared(lengths, groups, G, Hkv=2, P=16, kv="bf16", seed=0):
