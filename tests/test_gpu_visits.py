@@ -22,7 +22,8 @@ from variable_length_kv_amd import lib as L
 from variable_length_kv_amd import workloads as wl
 from variable_length_kv_amd.trace import DeviceTrace
 
-from gpu_helpers import dev, device_inputs, run
+from gpu_helpers import dev, device_inputs, run, shape_for
+from test_gpu_random_shapes import draw
 
 pytestmark = pytest.mark.gpu
 
@@ -201,3 +202,43 @@ def test_trace_every_step():
             if s == tr.steps - 1:
                 break
             dt.advance()
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shapes_every_row_once(seed):
+    """The random shapes of the parity test (head groupings 1-16, 1-8 kv heads,
+    pages of 16-256 tokens, tiles of 64-256, 1-1500 workgroups, all three
+    modes, both cache types, empty and page-boundary lengths): both launch
+    forms consume every live row exactly once."""
+    c, mode, T, W, S = draw(seed)
+    t = device_inputs(c)
+    for fused in (False, True):
+        got = _counted_run(c, mode, fused, W, S=S, T=T, t=t)
+        _same(got, _plain_run(c, mode, fused, W, S=S, T=T, t=t), f"random shape {seed}")
+
+
+def test_allocation_free_step_every_row_once():
+    """attn_step_noalloc (the library's per-GPU scratch instead of a
+    workspace) on a large batch, then a smaller one of another shape, then the
+    large one again: the scratch keeps the last call's contents, and each call
+    must still consume every live row exactly once."""
+    rng = np.random.default_rng(9)
+    big = wl.make_case("na-big", rng.integers(1, 9000, 40).astype(np.int32), Hq=64, Hkv=8, P=64, seed=1)
+    small = wl.make_case("na-small", np.array([0, 5, 700, 64, 17, 300], np.int32), Hq=16, Hkv=2, P=16,
+                         kv_dtype="fp8", seed=2)
+    for case, W in ((big, None), (small, 29), (big, None)):
+        t = device_inputs(case)
+        sh = shape_for(case, L.ATTN_DYNAMIC, W=W)
+        stride = case.pt_stride * case.P
+        tok, outc = _counters(case.B, case.Hq, case.Hkv, stride)
+        out = torch.empty_like(t["q"])
+        lse = torch.empty((case.B, case.Hq), dtype=torch.float32, device=dev())
+        status = torch.zeros(1, dtype=torch.int32, device=dev())
+        torch.cuda.synchronize()
+        with L.counting_visits(tok, stride, outc):
+            L.attn_step_noalloc(sh, t["q"], t["k"], t["v"], t["ks"], t["vs"], t["pt"], t["len"], case.sm_scale,
+                                out, lse, status)
+            torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        _check_counts(tok, outc, _expected_rows(case.lengths, case.Hkv, stride, stride), case.B, case.Hq,
+                      f"attn_step_noalloc {case.name}")
