@@ -242,3 +242,38 @@ def test_allocation_free_step_every_row_once():
         assert int(status.item()) == 0
         _check_counts(tok, outc, _expected_rows(case.lengths, case.Hkv, stride, stride), case.B, case.Hq,
                       f"attn_step_noalloc {case.name}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_limits_every_row_once(kv):
+    """The largest shapes: 8192 requests (one in ten empty) with 16 query heads
+    on one kv head, dynamic and static, both launch forms; 1024-token pages
+    under 256-token tiles; tiles of 1024 tokens; 65536 workgroups for a few
+    dozen units."""
+    rng = np.random.default_rng(11)
+    lengths = rng.integers(1, 160, 8192)
+    lengths[rng.random(8192) < 0.1] = 0
+    c = wl.make_case("max_batch", lengths, Hq=16, Hkv=1, P=16, kv_dtype=kv, seed=11)
+    t = device_inputs(c)
+    for fused in (False, True):
+        _counted_run(c, L.ATTN_DYNAMIC, fused, 512, t=t)
+        _counted_run(c, L.ATTN_STATIC, fused, 512, S=2, t=t)
+    big = wl.make_case("big_pages", [1, 63, 64, 65, 1023, 1024, 1025, 3000, 5000, 0, 2048], Hq=8, Hkv=2, P=1024,
+                       kv_dtype=kv, seed=13)
+    tiles = wl.make_case("big_tiles", [1024, 1025, 2047, 4100, 7, 0, 3333], Hq=16, Hkv=2, P=32, kv_dtype=kv, seed=14)
+    few = wl.make_case("few_units", [5, 300, 129, 0, 64], Hq=8, Hkv=1, P=16, kv_dtype=kv, seed=15)
+    for case, T, W in ((big, 256, 64), (tiles, 1024, 5), (few, 64, 1 << 16)):
+        tc = device_inputs(case)
+        for fused in (False, True):
+            _counted_run(case, L.ATTN_DYNAMIC, fused, W, T=T, t=tc)
+
+
+def test_limits_shared_items_beyond_lds():
+    """8192 requests in groups of 4 sharing a 64-token prefix: more plan items
+    than the shared planner's LDS copy of the tile prefix holds."""
+    rng = np.random.default_rng(12)
+    lengths = rng.integers(65, 140, 8192)
+    groups = [(4 * i, 4, 4) for i in range(8192 // 4)]
+    c = wl.make_shared_case("max_batch_shared", lengths, groups, Hq=4, Hkv=1, P=16, seed=12)
+    t = device_inputs(c)
+    _counted_run(c, L.ATTN_SHARED, False, 512, t=t)
